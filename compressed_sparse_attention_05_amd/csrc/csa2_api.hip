@@ -1,0 +1,245 @@
+// C-ABI entry points of libcsa2 (declared in include/csa2.h): argument
+// validation on the host, workspace sizing, and stream-ordered launches.
+// Nothing here allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/csa2.h"
+#include "csa2_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return CSA2_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(CSA2_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int dt) { return dt == CSA2_F32 || dt == CSA2_BF16; }
+size_t dtype_size(int dt) { return dt == CSA2_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_version(void) { return "csa2-mi355x 0.1 (gfx950)"; }
+
+const char* csa2_last_error(void) { return g_last_error.c_str(); }
+
+// --------------------------------------------------------------------------
+int mxfp4_kv_write(const void* x, int x_dtype, int64_t n_rows, int32_t D, const int64_t* dst_row,
+                   int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const void* idx_k_rows,
+                   int idx_k_dtype, int32_t d_I, void* idx_k_cache, void* stream) {
+    if (n_rows < 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: n_rows < 0");
+    if (D <= 0 || D % 16 != 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: D=%d must be a positive multiple of 16", D);
+    if (!valid_dtype(x_dtype)) return fail(CSA2_E_INVALID, "mxfp4_kv_write: bad x_dtype %d", x_dtype);
+    if (n_cache_rows < 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: n_cache_rows < 0");
+    if (n_rows == 0) return ok();
+    if (!x || !dst_row || !codes || !scales) return fail(CSA2_E_INVALID, "mxfp4_kv_write: null pointer");
+    if (!aligned(x, 16) || !aligned(codes, 8))
+        return fail(CSA2_E_INVALID, "mxfp4_kv_write: x must be 16-byte and codes 8-byte aligned");
+    if (idx_k_rows) {
+        if (!idx_k_cache) return fail(CSA2_E_INVALID, "mxfp4_kv_write: idx_k_cache is null");
+        if (!valid_dtype(idx_k_dtype)) return fail(CSA2_E_INVALID, "mxfp4_kv_write: bad idx_k_dtype");
+        const int64_t rb = static_cast<int64_t>(d_I) * static_cast<int64_t>(dtype_size(idx_k_dtype));
+        if (d_I <= 0 || rb % 4 != 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: indexer row bytes must be a positive multiple of 4");
+        if (!aligned(idx_k_rows, 4) || !aligned(idx_k_cache, 4))
+            return fail(CSA2_E_INVALID, "mxfp4_kv_write: indexer rows must be 4-byte aligned");
+    }
+    hipError_t e = csa2::launch_kv_quantize(x, x_dtype == CSA2_BF16, n_rows, D, dst_row, n_cache_rows,
+                                            codes, scales, as_stream(stream));
+    if (e != hipSuccess) return device_status(e, "mxfp4_kv_write");
+    if (idx_k_rows) {
+        const int64_t rb = static_cast<int64_t>(d_I) * static_cast<int64_t>(dtype_size(idx_k_dtype));
+        e = csa2::launch_row_copy(idx_k_rows, n_rows, rb, dst_row, n_cache_rows, idx_k_cache,
+                                  as_stream(stream));
+    }
+    return device_status(e, "mxfp4_kv_write");
+}
+
+// --------------------------------------------------------------------------
+static int check_score_args(const csa2_score_args* a) {
+    if (!a) return fail(CSA2_E_INVALID, "csa2_index_score: args is null");
+    if (a->B < 0 || a->Tq < 0 || a->cap < 0) return fail(CSA2_E_INVALID, "csa2_index_score: negative size");
+    if (!valid_dtype(a->q_dtype) || !valid_dtype(a->k_dtype))
+        return fail(CSA2_E_INVALID, "csa2_index_score: bad dtype");
+    if (a->H_I <= 0 || a->d_I <= 0) return fail(CSA2_E_INVALID, "csa2_index_score: H_I and d_I must be positive");
+    if (!csa2::score_shape_supported(a->H_I, a->d_I))
+        return fail(CSA2_E_UNSUPPORTED, "csa2_index_score: (H_I=%d, d_I=%d) not instantiated (have 8x128, 4x64, 2x32)",
+                    a->H_I, a->d_I);
+    if (a->m < 1) return fail(CSA2_E_INVALID, "csa2_index_score: m must be >= 1");
+    if (a->ld_scores < 0) return fail(CSA2_E_INVALID, "csa2_index_score: ld_scores < 0");
+    if (a->pool_blocks) {
+        if (a->P_b <= 0) return fail(CSA2_E_INVALID, "csa2_index_score: P_b must be positive");
+        if (a->ld_scores < static_cast<int64_t>(a->P_b) * 8)
+            return fail(CSA2_E_INVALID, "csa2_index_score: ld_scores must be >= 8*P_b in pool mode");
+        if (a->block_max) return fail(CSA2_E_INVALID, "csa2_index_score: block_max is for Full mode only");
+    }
+    if (a->B * a->Tq == 0) return CSA2_OK;
+    if (!a->q_idx || !a->w || !a->k_idx || !a->ctx_len || !a->scores)
+        return fail(CSA2_E_INVALID, "csa2_index_score: null pointer");
+    if (!aligned(a->k_idx, 16)) return fail(CSA2_E_INVALID, "csa2_index_score: k_idx must be 16-byte aligned");
+    return CSA2_OK;
+}
+
+size_t csa2_index_score_workspace_size(const csa2_score_args* a) {
+    if (!a || a->B < 0 || a->Tq < 0 || a->H_I <= 0 || a->d_I <= 0) return 0;
+    const size_t bytes = static_cast<size_t>(a->B * a->Tq) * static_cast<size_t>(a->H_I) *
+                         static_cast<size_t>(a->d_I) * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+int csa2_index_score(const csa2_score_args* a, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_score_args(a);
+    if (rc != CSA2_OK) return rc;
+    if (a->B * a->Tq == 0 || a->ld_scores == 0) return ok();
+    const size_t need = csa2_index_score_workspace_size(a);
+    if (!ws || ws_bytes < need)
+        return fail(CSA2_E_WORKSPACE, "csa2_index_score: workspace %zu bytes < required %zu", ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(CSA2_E_INVALID, "csa2_index_score: workspace must be 16-byte aligned");
+    csa2::ScoreLaunch p;
+    p.q_idx = a->q_idx; p.q_bf16 = a->q_dtype == CSA2_BF16;
+    p.w = a->w; p.k_idx = a->k_idx; p.k_bf16 = a->k_dtype == CSA2_BF16;
+    p.B = a->B; p.Tq = a->Tq; p.cap = a->cap; p.H_I = a->H_I; p.d_I = a->d_I;
+    p.ctx_len = a->ctx_len; p.q_pos = a->q_pos; p.m = a->m;
+    p.pool = a->pool_blocks; p.P_b = a->pool_blocks ? a->P_b : 0;
+    p.scores = a->scores; p.ld = a->ld_scores;
+    p.block_max = a->block_max; p.ld_bm = (a->ld_scores + 7) / 8;
+    p.qT = static_cast<float*>(ws);
+    return device_status(csa2::launch_score(p, as_stream(stream)), "csa2_index_score");
+}
+
+// --------------------------------------------------------------------------
+size_t csa2_topk_workspace_size(int64_t rows, int64_t n, int32_t k) {
+    (void)rows; (void)n; (void)k;
+    return 0;
+}
+
+int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int32_t k,
+              const int32_t* pool_blocks, int32_t P_b, int32_t* out_idx, void* ws, size_t ws_bytes,
+              void* stream) {
+    (void)ws; (void)ws_bytes;
+    if (rows < 0 || n < 0 || ld < n) return fail(CSA2_E_INVALID, "csa2_topk: need rows >= 0 and 0 <= n <= ld");
+    if (k <= 0) return fail(CSA2_E_INVALID, "csa2_topk: k must be positive");
+    if (n > (int64_t(1) << 31) - 1) return fail(CSA2_E_UNSUPPORTED, "csa2_topk: n above 2^31-1");
+    if (pool_blocks && (P_b <= 0 || n != static_cast<int64_t>(P_b) * 8))
+        return fail(CSA2_E_INVALID, "csa2_topk: with pool_blocks, n must equal 8*P_b");
+    if (rows == 0) return ok();
+    if (!scores || !out_idx) return fail(CSA2_E_INVALID, "csa2_topk: null pointer");
+    return device_status(csa2::launch_topk(scores, rows, n, ld, k, pool_blocks, P_b, out_idx, as_stream(stream)),
+                         "csa2_topk");
+}
+
+size_t csa2_build_candidate_pool_workspace_size(int64_t rows, int64_t n_blocks, int32_t P_b) {
+    return csa2_topk_workspace_size(rows, n_blocks, P_b);
+}
+
+int csa2_build_candidate_pool(const float* block_max, int64_t rows, int64_t n_blocks, int64_t ld,
+                              int32_t P_b, int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream) {
+    if (P_b <= 0) return fail(CSA2_E_INVALID, "csa2_build_candidate_pool: P_b must be positive");
+    int rc = csa2_topk(block_max, rows, n_blocks, ld, P_b, nullptr, 0, out_blocks, ws, ws_bytes, stream);
+    if (rc != CSA2_OK) {
+        std::string m = "csa2_build_candidate_pool: " + g_last_error;
+        g_last_error = m;
+    }
+    return rc;
+}
+
+// --------------------------------------------------------------------------
+static int check_attn_common(const char* fn, const void* q, int q_dtype, const uint8_t* codes,
+                             const uint8_t* scales, int64_t cap, const int32_t* idx, int32_t k,
+                             const void* swa, int swa_dtype, int32_t W, int64_t units, int32_t H,
+                             int32_t D, const float* out) {
+    if (units < 0 || cap < 0) return fail(CSA2_E_INVALID, "%s: negative size", fn);
+    if (k < 0 || W < 0 || k + W <= 0) return fail(CSA2_E_INVALID, "%s: need k >= 0, W >= 0, k + W > 0", fn);
+    if (!valid_dtype(q_dtype) || !valid_dtype(swa_dtype)) return fail(CSA2_E_INVALID, "%s: bad dtype", fn);
+    if (H <= 0 || D <= 0 || D % 16 != 0) return fail(CSA2_E_INVALID, "%s: bad H=%d or D=%d", fn, H, D);
+    if (!csa2::attn_shape_supported(H, D))
+        return fail(CSA2_E_UNSUPPORTED, "%s: (H=%d, D=%d) not instantiated (D=512 with H %% 64 == 0, or D=64 with H <= 64)",
+                    fn, H, D);
+    if (units == 0) return CSA2_OK;
+    if (!q || !out || (k > 0 && (!codes || !scales || !idx)) || (W > 0 && !swa))
+        return fail(CSA2_E_INVALID, "%s: null pointer", fn);
+    if (!aligned(q, 16) || !aligned(out, 16) || (swa && !aligned(swa, 16)) || (codes && !aligned(codes, 4)))
+        return fail(CSA2_E_INVALID, "%s: q/out/swa must be 16-byte and codes 4-byte aligned", fn);
+    return CSA2_OK;
+}
+
+size_t csa2_sparse_attn_decode_workspace_size(const csa2_attn_args* a) {
+    if (!a || a->B <= 0 || !csa2::attn_shape_supported(a->H, a->D)) return 0;
+    return csa2::attn_workspace_bytes(a->B, a->H, a->D, a->k, a->W);
+}
+
+int csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+    if (!a) return fail(CSA2_E_INVALID, "csa2_sparse_attn_decode: args is null");
+    int rc = check_attn_common("csa2_sparse_attn_decode", a->q, a->q_dtype, a->codes, a->scales, a->cap,
+                               a->idx, a->k, a->swa, a->swa_dtype, a->W, a->B, a->H, a->D, a->out);
+    if (rc != CSA2_OK) return rc;
+    if (a->B == 0) return ok();
+    if (a->W > 0 && !a->swa_len) return fail(CSA2_E_INVALID, "csa2_sparse_attn_decode: swa_len is null");
+    const size_t need = csa2_sparse_attn_decode_workspace_size(a);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(CSA2_E_WORKSPACE, "csa2_sparse_attn_decode: workspace %zu bytes < required %zu", ws_bytes, need);
+    if (ws && !aligned(ws, 16)) return fail(CSA2_E_INVALID, "csa2_sparse_attn_decode: workspace must be 16-byte aligned");
+    csa2::AttnLaunch L;
+    L.q = a->q; L.q_bf16 = a->q_dtype == CSA2_BF16;
+    L.codes = a->codes; L.scales = a->scales; L.cap = a->cap; L.kv_unit_stride = a->cap;
+    L.idx = a->idx; L.k = a->k;
+    L.swa = a->swa; L.swa_bf16 = a->swa_dtype == CSA2_BF16; L.W = a->W; L.swa_len = a->swa_len;
+    L.q_pos0 = 0; L.swa_start = 0; L.prefill = false;
+    L.units = a->B; L.H = a->H; L.D = a->D; L.sm_scale = a->sm_scale; L.out = a->out;
+    L.ws = need > 0 ? static_cast<float*>(ws) : nullptr; L.ws_bytes = ws_bytes;
+    return device_status(csa2::launch_attn(L, as_stream(stream)), "csa2_sparse_attn_decode");
+}
+
+size_t csa2_sparse_attn_prefill_workspace_size(const csa2_attn_prefill_args* a) {
+    if (!a || a->T <= 0 || !csa2::attn_shape_supported(a->H, a->D)) return 0;
+    return csa2::attn_workspace_bytes(a->T, a->H, a->D, a->k, a->W);
+}
+
+int csa2_sparse_attn_prefill(const csa2_attn_prefill_args* a, void* ws, size_t ws_bytes, void* stream) {
+    if (!a) return fail(CSA2_E_INVALID, "csa2_sparse_attn_prefill: args is null");
+    int rc = check_attn_common("csa2_sparse_attn_prefill", a->q, a->q_dtype, a->codes, a->scales, a->cap,
+                               a->idx, a->k, a->swa, a->swa_dtype, a->W, a->T, a->H, a->D, a->out);
+    if (rc != CSA2_OK) return rc;
+    if (a->T == 0) return ok();
+    if (a->q_pos0 < 0 || a->swa_start < 0) return fail(CSA2_E_INVALID, "csa2_sparse_attn_prefill: negative position");
+    const size_t need = csa2_sparse_attn_prefill_workspace_size(a);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(CSA2_E_WORKSPACE, "csa2_sparse_attn_prefill: workspace %zu bytes < required %zu", ws_bytes, need);
+    if (ws && !aligned(ws, 16)) return fail(CSA2_E_INVALID, "csa2_sparse_attn_prefill: workspace must be 16-byte aligned");
+    csa2::AttnLaunch L;
+    L.q = a->q; L.q_bf16 = a->q_dtype == CSA2_BF16;
+    L.codes = a->codes; L.scales = a->scales; L.cap = a->cap; L.kv_unit_stride = 0;
+    L.idx = a->idx; L.k = a->k;
+    L.swa = a->swa; L.swa_bf16 = a->swa_dtype == CSA2_BF16; L.W = a->W; L.swa_len = nullptr;
+    L.q_pos0 = a->q_pos0; L.swa_start = a->swa_start; L.prefill = true;
+    L.units = a->T; L.H = a->H; L.D = a->D; L.sm_scale = a->sm_scale; L.out = a->out;
+    L.ws = need > 0 ? static_cast<float*>(ws) : nullptr; L.ws_bytes = ws_bytes;
+    return device_status(csa2::launch_attn(L, as_stream(stream)), "csa2_sparse_attn_prefill");
+}
+
+}  // extern "C"

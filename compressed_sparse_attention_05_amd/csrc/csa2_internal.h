@@ -1,0 +1,57 @@
+// Internal declarations shared by the libcsa2 translation units (host side).
+// Not part of the public ABI (include/csa2.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// Launchers: return hipSuccess or the launch error.  Arguments are already
+// validated by the entry points in csa2_api.hip.
+hipError_t launch_kv_quantize(const void* x, bool x_bf16, int64_t n_rows, int D,
+                              const int64_t* dst_row, int64_t n_cache_rows, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st);
+hipError_t launch_row_copy(const void* src, int64_t n_rows, int64_t row_bytes,
+                           const int64_t* dst_row, int64_t n_cache_rows, void* dst,
+                           hipStream_t st);
+
+struct ScoreLaunch {
+    const void* q_idx; bool q_bf16;
+    const float* w;
+    const void* k_idx; bool k_bf16;
+    int64_t B, Tq, cap;
+    int H_I, d_I;
+    const int32_t* ctx_len;
+    const int64_t* q_pos;
+    int m;
+    const int32_t* pool; int P_b;
+    float* scores; int64_t ld;
+    float* block_max; int64_t ld_bm;
+    float* qT;   // workspace [B*Tq][d_I][H_I] float32
+};
+bool score_shape_supported(int H_I, int d_I);
+hipError_t launch_score(const ScoreLaunch& p, hipStream_t st);
+
+hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int k,
+                       const int32_t* pool, int P_b, int32_t* out, hipStream_t st);
+
+struct AttnLaunch {
+    const void* q; bool q_bf16;
+    const uint8_t* codes; const uint8_t* scales; int64_t cap;
+    int64_t kv_unit_stride;      // cache rows between consecutive units (cap or 0)
+    const int32_t* idx; int k;
+    const void* swa; bool swa_bf16; int W;
+    const int32_t* swa_len;      // decode: [units]; prefill: NULL
+    int64_t q_pos0, swa_start;   // prefill window geometry
+    bool prefill;
+    int64_t units; int H, D;
+    float sm_scale;
+    float* out;
+    float* ws; size_t ws_bytes;
+};
+bool attn_shape_supported(int H, int D);
+size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W);
+hipError_t launch_attn(const AttnLaunch& p, hipStream_t st);
+
+}  // namespace csa2

@@ -1,0 +1,213 @@
+/*
+ * csa2.h - C ABI of libcsa2, the MI355X (gfx950) CSA2 global-attention hot path.
+ *
+ * The path, per query (decode token or prefill token):
+ *   1. score the visible compressed KV with the sparse indexer (Full mode:
+ *      every visible entry; Reindex mode: the 16,384-position candidate pool),
+ *   2. select the top-k positions,
+ *   3. gather and dequantise the MXFP4 main KV of those positions,
+ *   4. append the layer's sliding-window (SWA) KV,
+ *   5. run one softmax attention over the joined set.
+ * Reuse layers skip 1-2 and pass the previous layer's index list to step 5.
+ *
+ * Sources (page title, section):
+ *   [KVC] "DeepSeek-V4.1-Flash KV Cache Compression" reading notes, sections 2-5.
+ *   [SUM] DeepSeek-V4.1-Flash summary page, "Methodology / Architecture Components".
+ *   [DR]  "DeepSeek-V4.1-Flash: reading a model through its three memory costs",
+ *         section 03 (mode table).
+ *   [THR] "Notes on DeepSeek V4.1 Flash" thread, posts 4-6.
+ *
+ * Conventions for every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller (row-major,
+ *     contiguous unless a leading dimension is given).  Argument structs and
+ *     scalars live on the host.  The library never allocates, frees or
+ *     synchronises: scratch comes from the caller's (ws, ws_bytes), sized by
+ *     the matching *_workspace_size call (0 means none is needed).
+ *   - `stream` is a hipStream_t passed as void* (NULL = legacy default
+ *     stream).  Work is enqueued asynchronously on it, on the current device.
+ *   - Return value: CSA2_OK, or an error code; csa2_last_error() then holds a
+ *     message (thread-local).  No C++ exception crosses the ABI.  Argument
+ *     errors are detected on the host before anything is enqueued.
+ *   - Data preconditions that live in device memory are not validated on the
+ *     host: inputs must be finite; index/position entries outside [0, cap)
+ *     are treated as empty (-1) by the kernels rather than read.
+ *   - Index lists are int32 entry positions, ascending, padded with -1.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum csa2_status {
+    CSA2_OK = 0,
+    CSA2_E_INVALID = 1,     /* null pointer, bad shape or size, bad dtype value */
+    CSA2_E_UNSUPPORTED = 2, /* shape valid in principle but not instantiated here */
+    CSA2_E_WORKSPACE = 3,   /* ws is NULL or ws_bytes below the *_workspace_size value */
+    CSA2_E_DEVICE = 4       /* a HIP launch or runtime call failed */
+};
+
+enum csa2_dtype { CSA2_F32 = 0, CSA2_BF16 = 1 };
+
+const char *csa2_version(void);
+const char *csa2_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * mxfp4_kv_write - quantise main-KV rows into the MXFP4 cache and append
+ * indexer-K rows.  Format ([KVC] section 4; [SUM] item 5): per block of 16
+ * consecutive channels one E4M3 scale byte (OCP FN encoding, sign 0) and 16
+ * E2M1 nibbles; no second-level scale.
+ *   scale = E4M3 value nearest to amax/6 (ties to the even code, saturating
+ *           at 448; amax = largest |x| of the block),
+ *   code  = E2M1 value nearest to |x|/scale (ties to even, saturating at 6),
+ *           sign bit set only for a nonzero negative code; a scale of 0
+ *           gives all-zero codes.
+ *   Channel 2j is the low nibble of code byte j.
+ *
+ * x          [n_rows][D] (x_dtype: CSA2_F32 or CSA2_BF16)
+ * dst_row    [n_rows] int64, flat destination row b*cap + pos; rows outside
+ *            [0, n_cache_rows) are skipped
+ * codes      [n_cache_rows][D/2] uint8   (written at dst rows)
+ * scales     [n_cache_rows][D/16] uint8  (written at dst rows)
+ * idx_k_rows [n_rows][d_I] (idx_k_dtype) or NULL; when given, row i is
+ *            copied unchanged to idx_k_cache[dst_row[i]] ([n_cache_rows][d_I]).
+ * Requires D % 16 == 0, n_rows >= 0.
+ * ------------------------------------------------------------------------ */
+int mxfp4_kv_write(const void *x, int x_dtype, int64_t n_rows, int32_t D,
+                   const int64_t *dst_row, int64_t n_cache_rows, uint8_t *codes, uint8_t *scales,
+                   const void *idx_k_rows, int idx_k_dtype, int32_t d_I, void *idx_k_cache,
+                   void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_index_score - sparse-indexer scores ([KVC] sections 2-3; [DR] 03).
+ * The pages give no score formula; this library fixes
+ *     s_t = sum_h w_h * ReLU(q_h . k_t)
+ * with one indexer key per position shared by all H_I heads, in float32 as
+ * ordered fma chains (bf16 inputs widened exactly):
+ *     d_h = +0; for c in 0..d_I-1: d_h = fma(q[h][c], k_t[c], d_h)
+ *     s   = +0; for h in 0..H_I-1: s = fma(w[h], d_h > 0 ? d_h : +0, s)
+ * so the scores, and every index chosen from them, are bit-reproducible.
+ *
+ * A query row is (b, t).  Its visible entry count is
+ *     vis = ctx_len[b]                                   (q_pos == NULL)
+ *     vis = min(ctx_len[b], floor((q_pos[b][t] + 1) / m)) (q_pos given:
+ *           only complete m-token blocks are visible, [KVC] section 2)
+ * Full mode (pool_blocks == NULL): scores[row][j] for j < ld_scores is s_j
+ *     when j < vis, else -inf.  If block_max != NULL it also writes
+ *     block_max[row][b] for b < ceil(ld_scores/8): the largest visible score
+ *     in positions [8b, 8b+8) (-inf if none; zero reported as +0), the input
+ *     of csa2_build_candidate_pool ([KVC] section 3, step 1).
+ * Reindex mode (pool_blocks != NULL, [P_b] per row, ascending, -1 padded):
+ *     scores[row][s] for s < 8*P_b scores position 8*pool[s/8] + s%8, or
+ *     -inf when the block id is -1 or the position is not visible.
+ *     ld_scores must be >= 8*P_b; block_max must be NULL.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_score_args {
+    const void *q_idx;  int32_t q_dtype;  /* [B][Tq][H_I][d_I] */
+    const float *w;                       /* [B][Tq][H_I] */
+    const void *k_idx;  int32_t k_dtype;  /* [B][cap][d_I] indexer-K cache */
+    int64_t B, Tq, cap;
+    int32_t H_I, d_I;
+    const int32_t *ctx_len;               /* [B] */
+    const int64_t *q_pos;                 /* [B][Tq] or NULL */
+    int32_t m;                            /* tokens per entry (>= 1) */
+    const int32_t *pool_blocks;           /* [B][Tq][P_b] or NULL */
+    int32_t P_b;
+    float *scores;  int64_t ld_scores;    /* [B][Tq][ld_scores] */
+    float *block_max;                     /* [B][Tq][ceil(ld_scores/8)] or NULL */
+} csa2_score_args;
+
+size_t csa2_index_score_workspace_size(const csa2_score_args *a);
+int csa2_index_score(const csa2_score_args *a, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_topk - exact top-k per row ([KVC] sections 2-3): order by score
+ * descending, then slot ascending (-0 equals +0); -inf slots are never
+ * chosen.  Writes min(k, #finite) entries in ascending order, then -1.
+ * scores     [rows][ld] float32, n <= ld slots per row
+ * pool_blocks NULL: the output entry is the slot itself (a position).
+ *            else [rows][P_b] ascending block ids: slot s is position
+ *            8*pool[row][s/8] + s%8 (n must equal 8*P_b), so slot order is
+ *            position order and ties go to the lower position.
+ * out_idx    [rows][k] int32
+ * ------------------------------------------------------------------------ */
+size_t csa2_topk_workspace_size(int64_t rows, int64_t n, int32_t k);
+int csa2_topk(const float *scores, int64_t rows, int64_t n, int64_t ld, int32_t k,
+              const int32_t *pool_blocks, int32_t P_b, int32_t *out_idx,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_build_candidate_pool - the hierarchical indexer's pool ([KVC]
+ * section 3, steps 1-2; [SUM] item 3): the P_b blocks (2,048 on the pages)
+ * with the largest block maxima, ties to the lower block id, as ascending
+ * block ids padded with -1.  Pool positions are 8b..8b+7 of each block.
+ * block_max [rows][ld], n_blocks <= ld; out_blocks [rows][P_b].
+ * ------------------------------------------------------------------------ */
+size_t csa2_build_candidate_pool_workspace_size(int64_t rows, int64_t n_blocks, int32_t P_b);
+int csa2_build_candidate_pool(const float *block_max, int64_t rows, int64_t n_blocks, int64_t ld,
+                              int32_t P_b, int32_t *out_blocks, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn_decode - gather, dequantise, join with SWA, attend
+ * ([DR] 03; [THR] post 4).  For each sequence b and head h:
+ *   rows  = [MXFP4 main rows idx[b][j] (j < k, entries -1 skipped)]
+ *           ++ [swa[b][r] for r < min(swa_len[b], W)]
+ *   z_j   = sm_scale * (q[b][h] . row_j);  p = softmax(z);  out = sum p_j row_j
+ * The latent is both key and value and all H heads read the same rows.
+ * An empty row set gives zeros.
+ * q     [B][H][D] bf16 (or f32); codes [B][cap][D/2], scales [B][cap][D/16];
+ * idx   [B][k] int32;  swa [B][W][D] bf16 (or f32);  swa_len [B] int32;
+ * out   [B][H][D] float32.
+ * Instantiated for D = 512 with H a multiple of 64, and for the small
+ * parity shape D = 64 with H <= 64 (else CSA2_E_UNSUPPORTED).
+ * Arithmetic: rows exactly in fp16 (every MXFP4 value is an fp16 number; q
+ * and SWA values in [2^-14, 65504] convert exactly), MFMA with float32
+ * accumulation, float32 softmax, probabilities rounded to fp16 for P.V.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_attn_args {
+    const void *q;  int32_t q_dtype;
+    const uint8_t *codes;  const uint8_t *scales;  int64_t cap;
+    const int32_t *idx;  int32_t k;
+    const void *swa;  int32_t swa_dtype;  int32_t W;  const int32_t *swa_len;
+    int64_t B;  int32_t H, D;
+    float sm_scale;
+    float *out;
+} csa2_attn_args;
+
+size_t csa2_sparse_attn_decode_workspace_size(const csa2_attn_args *a);
+int csa2_sparse_attn_decode(const csa2_attn_args *a, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn_prefill - the same per query token of one sequence's
+ * chunk.  Query t sits at token position i = q_pos0 + t and uses its own
+ * idx[t] row plus the window [max(swa_start, i - W + 1), i] ([KVC] section
+ * 5 writes the window as [max(s, i - n_win + 1), i]; swa_start = s, 0 when
+ * nothing was replayed).  The window buffer holds T + W - 1 rows; row r is
+ * token position q_pos0 - (W - 1) + r (rows before position 0 are unused).
+ * q [T][H][D]; codes [cap][D/2]; scales [cap][D/16]; idx [T][k];
+ * swa [T + W - 1][D]; out [T][H][D] float32.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_attn_prefill_args {
+    const void *q;  int32_t q_dtype;
+    const uint8_t *codes;  const uint8_t *scales;  int64_t cap;
+    const int32_t *idx;  int32_t k;
+    const void *swa;  int32_t swa_dtype;  int32_t W;
+    int64_t q_pos0, swa_start;
+    int64_t T;  int32_t H, D;
+    float sm_scale;
+    float *out;
+} csa2_attn_prefill_args;
+
+size_t csa2_sparse_attn_prefill_workspace_size(const csa2_attn_prefill_args *a);
+int csa2_sparse_attn_prefill(const csa2_attn_prefill_args *a, void *ws, size_t ws_bytes,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

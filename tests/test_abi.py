@@ -1,0 +1,79 @@
+"""The C-ABI library loads and exports every symbol include/csa2.h declares,
+and its host-side argument checks return the documented status codes
+(these calls return before any device work, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_05_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for n in ["mxfp4_kv_write", "csa2_index_score", "csa2_topk", "csa2_build_candidate_pool",
+              "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill", "csa2_last_error",
+              "csa2_version"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) <= set(binding.SIGNATURES)
+
+
+def test_version_string():
+    assert "gfx950" in binding.version()
+
+
+def _err():
+    return binding.lib().csa2_last_error().decode()
+
+
+def test_topk_rejects_bad_arguments_on_host():
+    L = binding.lib()
+    rc = L.csa2_topk(None, 4, 10, 10, 0, None, 0, None, None, 0, None)
+    assert rc == 1 and "k must be positive" in _err()
+    rc = L.csa2_topk(None, 4, 10, 5, 3, None, 0, None, None, 0, None)
+    assert rc == 1 and "ld" in _err()
+    rc = L.csa2_topk(ctypes.c_void_p(16), 1, 17, 17, 3, ctypes.c_void_p(16), 2, ctypes.c_void_p(16),
+                     None, 0, None)
+    assert rc == 1 and "8*P_b" in _err()
+    assert L.csa2_topk(None, 0, 10, 10, 3, None, 0, None, None, 0, None) == 0  # nothing to do
+
+
+def test_score_unsupported_shape_and_workspace():
+    L = binding.lib()
+    a = binding.ScoreArgs(q_idx=16, q_dtype=1, w=16, k_idx=16, k_dtype=1, B=1, Tq=1, cap=8, H_I=3,
+                          d_I=128, ctx_len=16, m=1, scores=16, ld_scores=8)
+    assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 2
+    a.H_I = 8
+    assert L.csa2_index_score_workspace_size(ctypes.byref(a)) == 8 * 128 * 4
+    assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 3  # workspace missing
+    a.m = 0
+    assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 1
+
+
+def test_kv_write_and_attention_argument_checks():
+    L = binding.lib()
+    assert L.mxfp4_kv_write(None, 0, 1, 20, None, 1, None, None, None, 0, 0, None, None) == 1
+    assert "multiple of 16" in _err()
+    a = binding.AttnArgs(q=16, q_dtype=1, codes=16, scales=16, cap=4, idx=16, k=4, swa=16, swa_dtype=1,
+                         W=4, swa_len=16, B=1, H=48, D=512, sm_scale=0.1, out=16)
+    assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 2
+    a.H, a.D = 64, 40
+    assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 1
