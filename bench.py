@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--secondary]
+
+A step is one decode token for B sequences through the whole path of the
+workload's layer schedule: mxfp4_kv_write of the token's entry, the Full
+scan with fused block max, the candidate pool, top-k and the sparse
+attention (plus Reindex/Reuse layers where the schedule has them).  Inputs
+are seeded synthetic tensors (csa2_inputs) already resident in HBM; two
+independent input sets alternate so the 256 MiB MALL cannot serve a step
+from the previous one.
+
+Prints ONE JSON line: queries/s for the workload, the dominant kernel's
+roofline (the Full-mode indexer scan, timed live with HIP events on the
+stream it runs on), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import csa2_inputs as ci  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "CSA2 decode queries/s & achieved HBM GB/s at 128K and 1M ctx (1 GPU)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_scan_traffic.json")
+
+
+# --------------------------------------------------------------------------
+def fill_kv_cache(K, codes, scales, seed, n_valid, D, chunk_rows=1 << 16):
+    """Quantise generated main-KV rows [b][0..n_valid) into the MXFP4 cache
+    with the library's writer (cache build, untimed)."""
+    B, cap, _ = codes.shape
+    dev = codes.device
+    for b in range(B):
+        for p0 in range(0, n_valid, chunk_rows):
+            p1 = min(n_valid, p0 + chunk_rows)
+            rows = torch.arange(b * cap + p0, b * cap + p1, device=dev, dtype=torch.int64)
+            x = ci.gaussian_rows(seed, ci.TID_KV, rows, D, dtype=torch.bfloat16, clip=ci.NORM_BOUND)
+            K.mxfp4_kv_write(x, rows, codes, scales)
+
+
+class InputSet:
+    """One complete set of decode inputs for a workload, on the GPU."""
+
+    def __init__(self, K, w: ci.Workload, seed: int, dev):
+        from compressed_sparse_attention_05_amd.decode import DecodeCache, LayerInputs
+        B, N, D, d_I, H_I, H, W = w.B, w.N, w.D, w.d_I, w.H_I, w.H, w.W
+        cap = N
+        self.seed = seed
+        self.codes = torch.empty((B, cap, D // 2), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((B, cap, D // 16), dtype=torch.uint8, device=dev)
+        fill_kv_cache(K, self.codes, self.scales, seed, N - 1, D)
+        # indexer keys: generated row-major (flat index (b*cap + pos)*d_I + c),
+        # stored in the library's tiled layout
+        self.k_idx = torch.empty((B, cap, d_I), dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            rows = torch.empty((1, cap, d_I), dtype=torch.bfloat16, device=dev)
+            ci.fill_gaussian_(rows, seed, ci.TID_K_IDX, first=b * cap * d_I)
+            self.k_idx[b] = K.tile_indexer_cache(rows)[0]
+            del rows
+        self.cache = DecodeCache(self.codes, self.scales, self.k_idx,
+                                 torch.full((B,), N, dtype=torch.int32, device=dev),
+                                 torch.full((B,), W, dtype=torch.int32, device=dev))
+        # the token written by the step: entry N-1 of every sequence
+        self.dst_row = torch.arange(B, device=dev, dtype=torch.int64) * cap + (N - 1)
+        self.new_kv = ci.gaussian_rows(seed, ci.TID_KV, self.dst_row, D, dtype=torch.bfloat16,
+                                       clip=ci.NORM_BOUND)
+        self.new_kidx = ci.gaussian_rows(seed, ci.TID_K_IDX, self.dst_row, d_I, dtype=torch.bfloat16)
+        self.layers = []
+        for li, mode in enumerate(w.schedule):
+            q = ci.gaussian(seed, ci.layer_tid(ci.TID_Q, li), (B, H, D), torch.bfloat16, dev)
+            swa = ci.gaussian(seed, ci.layer_tid(ci.TID_SWA, li), (B, W, D), torch.bfloat16, dev)
+            qi = wt = None
+            if mode in "FX":
+                qi = ci.gaussian(seed, ci.layer_tid(ci.TID_Q_IDX, li), (B, 1, H_I, d_I), torch.bfloat16, dev)
+                wt = ci.uniform(seed, ci.layer_tid(ci.TID_W, li), (B, 1, H_I), dev)
+            self.layers.append(LayerInputs(q=q, swa=swa, q_idx=qi, w=wt))
+
+
+def make_step(K, w: ci.Workload, s: InputSet, pool=None):
+    from compressed_sparse_attention_05_amd.decode import DecodeStep
+    has_full = "F" in w.schedule
+    return DecodeStep(w.schedule, s.cache, s.layers, k=w.k, P_b=w.P_b,
+                      new_kv=s.new_kv if has_full else None,
+                      new_kidx=s.new_kidx if has_full else None,
+                      dst_row=s.dst_row if has_full else None, pool=pool)
+
+
+def build_pool_for(K, w: ci.Workload, s: InputSet):
+    """Reindex workloads: the pool comes from a preceding Full layer (untimed)."""
+    from compressed_sparse_attention_05_amd.decode import DecodeStep, LayerInputs
+    dev = s.codes.device
+    qi = ci.gaussian(s.seed, ci.layer_tid(ci.TID_Q_IDX, 63), (w.B, 1, w.H_I, w.d_I), torch.bfloat16, dev)
+    wt = ci.uniform(s.seed, ci.layer_tid(ci.TID_W, 63), (w.B, 1, w.H_I), dev)
+    full = LayerInputs(q=s.layers[0].q, swa=s.layers[0].swa, q_idx=qi, w=wt)
+    st = DecodeStep("F", s.cache, [full], k=w.k, P_b=w.P_b, new_kv=s.new_kv, new_kidx=s.new_kidx,
+                    dst_row=s.dst_row)
+    st.run()
+    torch.cuda.synchronize()
+    return st.pool.clone()
+
+
+# --------------------------------------------------------------------------
+def algorithmic_bytes_per_query(w: ci.Workload):
+    """Bytes the method must move per query (one sequence, one step):
+    indexer keys scanned, selected rows gathered (288 B MXFP4 each), window
+    rows, queries, outputs, index lists.  Score scratch and re-reads excluded."""
+    D, d_I = w.D, w.d_I
+    row = D // 2 + D // 16
+    per_layer_attn = w.k * row + w.W * D * 2 + w.H * D * 2 + w.H * D * 4 + w.k * 4
+    idx_q = w.H_I * d_I * 2 + w.H_I * 4
+    total = 0
+    for mode in w.schedule:
+        if mode == "F":
+            total += w.N * d_I * 2 + idx_q
+        elif mode == "X":
+            total += w.P_b * 8 * d_I * 2 + w.P_b * 4 + idx_q
+        total += per_layer_attn
+    if "F" in w.schedule:
+        total += row + d_I * 2 + D * 2 + d_I * 2   # the written entry (read + write)
+    return total
+
+
+def scan_bytes_per_launch(w: ci.Workload):
+    """Full scan (dominant kernel): indexer-K rows of every visible entry plus
+    the indexer queries and head weights, for the B rows of one launch."""
+    return w.B * (w.N * w.d_I * 2 + w.H_I * w.d_I * 2 + w.H_I * 4)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("score.hip",):
+        with open(os.path.join(ROOT, "compressed_sparse_attention_05_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload_name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+def run_workload(K, w: ci.Workload, steps: int, warmup: int, dev):
+    sets = [InputSet(K, w, w.seed + 100 * i, dev) for i in range(2)]
+    pools = [build_pool_for(K, w, s) if "X" in w.schedule and "F" not in w.schedule else None
+             for s in sets]
+    runners = [make_step(K, w, s, pool=p) for s, p in zip(sets, pools)]
+    torch.cuda.synchronize()
+    scan_name = next((f"score{i}" for i, m in enumerate(w.schedule) if m == "F"), None)
+    if scan_name is None:
+        scan_name = next(f"score{i}" for i, m in enumerate(w.schedule) if m == "X")
+    for i in range(warmup):
+        runners[i % 2].run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        runners[i % 2].run(events={scan_name: evs[i]})
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return dict(sets=sets, runners=runners, ms_per_step=ms_step, wall_s=wall, scan_ms=scan_ms,
+                scan_name=scan_name)
+
+
+def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
+    """The oracle, as it stands, on n_queries sequences of the workload's
+    first Full layer (write + scan + block max + pool + top-k + attention),
+    single-threaded.  Returns queries/s and what was sampled."""
+    import numpy as np
+    import oracle
+    import compressed_sparse_attention_05_amd as K
+
+    B, N, D = w.B, w.N, w.D
+    lay = s.layers[0]
+    t_total = 0.0
+    for b in range(n_queries):
+        kc = K.untile_indexer_cache(s.k_idx[b:b + 1])[0].cpu()   # generator output
+        qi, wt = lay.q_idx[b, 0].cpu(), lay.w[b, 0].cpu()
+        q, swa = lay.q[b].cpu(), lay.swa[b].cpu()
+        new_kv = s.new_kv[b:b + 1].cpu()
+        kc_f = oracle.as_f32(kc)
+        kc_f[N - 1] = oracle.as_f32(s.new_kidx[b:b + 1].cpu())[0]
+        t0 = time.perf_counter()
+        oracle.mxfp4_encode(new_kv)
+        sc = oracle.full_scores(qi, wt, kc_f, N, N)
+        bm = oracle.block_max(sc, N, (N + 7) // 8)
+        oracle.candidate_pool(bm, w.P_b)
+        idx = oracle.topk(sc, w.k)
+        t_total += time.perf_counter() - t0
+        # cache rows the attention reads: encoded by the oracle from the
+        # generator (the cache was built before this step; untimed)
+        sel = torch.from_numpy(idx[idx >= 0].astype(np.int64))
+        raw = ci.gaussian_rows(s.seed, ci.TID_KV, b * N + sel, D, dtype=torch.bfloat16,
+                               clip=ci.NORM_BOUND)
+        codes = np.zeros((N, D // 2), np.uint8)
+        scales = np.zeros((N, D // 16), np.uint8)
+        c, sc_ = oracle.mxfp4_encode(raw)
+        codes[sel.numpy()], scales[sel.numpy()] = c, sc_
+        if (sel == N - 1).any():
+            c1, s1 = oracle.mxfp4_encode(new_kv)
+            codes[N - 1], scales[N - 1] = c1[0], s1[0]
+        t0 = time.perf_counter()
+        oracle.attn_decode(q, codes, scales, idx, swa, w.W, 1.0 / math.sqrt(D))
+        t_total += time.perf_counter() - t0
+    return n_queries / t_total, t_total
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=ci.DECODE_128K.name, choices=sorted(ci.WORKLOADS))
+    ap.add_argument("--cpu-queries", type=int, default=4, help="oracle sample size (0 = skip)")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the 1M-context decode workloads (extra setup time)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(decode shards by sequence across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    import compressed_sparse_attention_05_amd as K
+    K.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = ci.WORKLOADS[args.workload]
+    if "F" not in w.schedule:
+        print("bench.py: the headline workload must contain a Full layer", file=sys.stderr)
+        return 2
+
+    print(f"# setting up {w.name}", file=sys.stderr, flush=True)
+    r = run_workload(K, w, args.steps, args.warmup, dev)
+    ms = r["ms_per_step"]
+    qps = w.B / (ms * 1e-3)
+    alg_q = algorithmic_bytes_per_query(w)
+    scan_bytes = scan_bytes_per_launch(w)
+    scan_gbs = scan_bytes / (r["scan_ms"] * 1e-3) / 1e9
+    traffic = traffic_for(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based Gaussian/uniform; MXFP4 KV, bf16 indexer K, Q, SWA)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.N, "schedule": w.schedule,
+                   "top_k": w.k, "window": w.W, "heads": w.H, "latent": w.D,
+                   "indexer": f"{w.H_I}x{w.d_I} bf16", "pool_blocks": w.P_b},
+        "algorithmic_GBps": round(alg_q * w.B / (ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "score_kernel (Full-mode indexer scan, incl. its q-transpose launch)",
+            "bound": "hbm",
+            "achieved": round(scan_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "scan_us": round(r["scan_ms"] * 1e3, 2),
+            "bytes_per_launch": scan_bytes,
+        },
+    }
+    if args.cpu_queries > 0:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        cps, secs = cpu_baseline(w, r["sets"][0], args.cpu_queries)
+        result["cpu_baseline"] = {
+            "value": round(cps, 4), "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{args.cpu_queries} of {w.B} sequences of {w.name} (full work each: write, "
+                      f"scan of {w.N} entries, block max, pool, top-{w.k}, attention), "
+                      f"{secs:.1f} s single-threaded",
+        }
+    if args.secondary:
+        sec = []
+        for name in (ci.DECODE_1M_BLOCK2.name,):
+            w2 = ci.WORKLOADS[name]
+            del r
+            torch.cuda.empty_cache()
+            print(f"# setting up {w2.name}", file=sys.stderr, flush=True)
+            r = run_workload(K, w2, max(20, args.steps // 4), 5, dev)
+            ms2 = r["ms_per_step"]
+            sec.append({"workload": w2.name, "value": round(w2.B / (ms2 * 1e-3), 1), "unit": "queries/s",
+                        "ms_per_step": round(ms2, 4),
+                        "algorithmic_GBps": round(algorithmic_bytes_per_query(w2) * w2.B / (ms2 * 1e-3) / 1e9, 1)})
+        result["secondary"] = sec
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -55,6 +55,7 @@ SIGNATURES = {
     "csa2_topk": (ctypes.c_int, [P, i64, i64, i64, i32, P, i32, P, P, ctypes.c_size_t, P]),
     "csa2_build_candidate_pool_workspace_size": (ctypes.c_size_t, [i64, i64, i32]),
     "csa2_build_candidate_pool": (ctypes.c_int, [P, i64, i64, i64, i32, P, P, ctypes.c_size_t, P]),
+    "csa2_topk_from_pool": (ctypes.c_int, [P, i64, i64, P, i32, i32, P, P]),
     "csa2_sparse_attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), P, ctypes.c_size_t, P]),
     "csa2_sparse_attn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnPrefillArgs)]),
@@ -125,6 +126,29 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 # --------------------------------------------------------------------------
+def tile_indexer_cache(k_rows: torch.Tensor) -> torch.Tensor:
+    """Row-major indexer keys [B][cap][d_I] -> the library's tiled layout
+    (returned with the same nominal shape).  Pure data movement: tile t of
+    64 flat rows stores 16-byte chunk c of row 64t+p at ((t*NCH + c)*64 + p)*16."""
+    B, cap, d_I = k_rows.shape
+    esz = k_rows.element_size()
+    cpc = 16 // esz
+    nch = d_I // cpc
+    if cap % 64 or (d_I * esz) % 16:
+        raise ValueError("tiled indexer cache needs cap % 64 == 0 and 16-byte rows")
+    t = k_rows.reshape(B, cap // 64, 64, nch, cpc).permute(0, 1, 3, 2, 4).contiguous()
+    return t.view(B, cap, d_I)
+
+
+def untile_indexer_cache(k_tiled: torch.Tensor) -> torch.Tensor:
+    """Inverse of tile_indexer_cache."""
+    B, cap, d_I = k_tiled.shape
+    cpc = 16 // k_tiled.element_size()
+    nch = d_I // cpc
+    t = k_tiled.reshape(B, cap // 64, nch, 64, cpc).permute(0, 1, 3, 2, 4).contiguous()
+    return t.view(B, cap, d_I)
+
+
 def mxfp4_kv_write(x, dst_row, codes, scales, idx_k_rows=None, idx_k_cache=None, stream=None):
     """Quantise rows x [n][D] into codes/scales at flat rows dst_row (int64),
     optionally copying idx_k_rows [n][d_I] into idx_k_cache."""
@@ -217,6 +241,20 @@ def csa2_build_candidate_pool(block_max, P_b: int = 2048, *, n_blocks: Optional[
     ws = _workspace(L.csa2_build_candidate_pool_workspace_size(rows, n_blocks, P_b), block_max.device)
     _check(L.csa2_build_candidate_pool(_ptr(block_max), rows, n_blocks, ld, P_b, _ptr(out), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def csa2_topk_from_pool(scores, pool_blocks, k: int, *, out=None, stream=None):
+    """Full-mode top-k of position-ordered scores [..., ld] through the
+    candidate pool [..., P_b] (k <= P_b); equals csa2_topk over the row."""
+    _dev(scores, "scores"); _dev(pool_blocks, "pool_blocks")
+    ld = scores.shape[-1]
+    rows = scores.numel() // ld if ld else 0
+    P_b = pool_blocks.shape[-1]
+    if out is None:
+        out = torch.empty((*scores.shape[:-1], k), dtype=torch.int32, device=scores.device)
+    _check(lib().csa2_topk_from_pool(_ptr(scores), rows, ld, _ptr(pool_blocks), P_b, k, _ptr(out),
+                                     _stream(stream)))
     return out
 
 

@@ -40,7 +40,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kKT = 32;          // keys per tile
-constexpr int kThreads = 256;
+constexpr int kMaxTilesPerSplit = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -93,26 +93,37 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return f16_bits(a) | (f16_bits(b) << 16);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
-    constexpr int DH = D / 2;              // channels per wave (S partial and O slice)
-    constexpr int SSTEPS = DH / 16;        // MFMA k-steps for S
-    constexpr int MT = DH / 32;            // O^T row tiles per wave
+// NQ = channel splits: the workgroup has 2*NQ waves; wave w owns head group
+// hg = w & 1 (32 heads) and channel slice dq = w >> 1 (D/NQ channels) for
+// both the S partial and its slice of O.
+template <int D, int NQ, bool BF16>
+__global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
+    constexpr int NW = 2 * NQ;             // waves
+    constexpr int NT = 64 * NW;            // threads
+    constexpr int DQ = D / NQ;             // channels per wave
+    constexpr int SSTEPS = DQ / 16;        // MFMA k-steps for the S partial
+    constexpr int MT = DQ / 32;            // O^T row tiles per wave
     constexpr int KROW = D + 8;            // padded Kt row (halves)
     constexpr int CH = D / 8;              // 8-channel chunks per row
-    // Kt is dead once S is formed, so the S partials ([4 waves][16][64]
-    // float32) reuse its space.
+    constexpr int KPT = kKT / NW;          // keys dequantised per thread
+    static_assert(DQ % 32 == 0 && (KPT == 4 || KPT == 8), "unsupported split");
+    // Kt is dead once S is formed, so the S partials ([NW][16][64] float32)
+    // reuse its space.
     constexpr int KT_BYTES = kKT * KROW * 2;
-    constexpr int SP_BYTES = 4 * 16 * 64 * 4;
+    constexpr int SP_BYTES = NW * 16 * 64 * 4;
     constexpr int KBUF = KT_BYTES > SP_BYTES ? KT_BYTES : SP_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[KBUF];
     __shared__ __attribute__((aligned(16))) _Float16 Vt[kKT * D];
-    __shared__ int kvalid[kKT];
+    __shared__ __attribute__((aligned(16))) int kvalid[kKT];
+    __shared__ int32_t idx_s[kKT * kMaxTilesPerSplit];
     _Float16* Kt = reinterpret_cast<_Float16*>(kbuf);
     float* Spart = reinterpret_cast<float*>(kbuf);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int hg = wv & 1, dh = wv >> 1;
+    // the wave index is uniform within a wave: make that explicit so every
+    // decision derived from it (key slot, channel slice) is a scalar branch
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hg = wv & 1, dq = wv >> 1;
     const int64_t u = blockIdx.x;
     const int split = blockIdx.y;
     const int hb = blockIdx.z;
@@ -139,30 +150,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     const int n_slots = a.k + a.W;
 
     // ---- q fragments (B operand of S^T): head = hbase + 32hg + lane%32,
-    // channels dh*DH + 16*st + 8*(lane/32) + 0..7
+    // channels dq*DQ + 16*st + 8*(lane/32) + 0..7
     half8 qf[SSTEPS];
     {
+        // loads from a clamped (always valid) head, masked afterwards, so no
+        // load sits in a lane-divergent branch
         const int head = hbase + 32 * hg + (lane & 31);
         const bool hv = head < a.H;
+        const int64_t qrow = (u * a.H + (hv ? head : 0)) * D;
+        uint4 raw[SSTEPS][BF16 ? 1 : 2];
 #pragma unroll
         for (int st = 0; st < SSTEPS; ++st) {
-            const int d0 = dh * DH + 16 * st + 8 * (lane >> 5);
-            uint32_t wd[4] = {0, 0, 0, 0};
-            if (hv) {
-                if (a.q_bf16) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(a.q + (u * a.H + head) * D + d0);
-                    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        wd[e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
-                } else {
-                    const float* qf32 = reinterpret_cast<const float*>(a.q) + (u * a.H + head) * D + d0;
-                    const float4 x0 = *reinterpret_cast<const float4*>(qf32);
-                    const float4 x1 = *reinterpret_cast<const float4*>(qf32 + 4);
-                    wd[0] = pack_h2(x0.x, x0.y); wd[1] = pack_h2(x0.z, x0.w);
-                    wd[2] = pack_h2(x1.x, x1.y); wd[3] = pack_h2(x1.z, x1.w);
-                }
+            const int d0 = dq * DQ + 16 * st + 8 * (lane >> 5);
+            if (BF16) {
+                raw[st][0] = *reinterpret_cast<const uint4*>(a.q + qrow + d0);
+            } else {
+                const float* qf32 = reinterpret_cast<const float*>(a.q) + qrow + d0;
+                raw[st][0] = *reinterpret_cast<const uint4*>(qf32);
+                raw[st][BF16 ? 0 : 1] = *reinterpret_cast<const uint4*>(qf32 + 4);
             }
+        }
+#pragma unroll
+        for (int st = 0; st < SSTEPS; ++st) {
+            uint32_t wd[4];
+            if (BF16) {
+                const uint32_t in[4] = {raw[st][0].x, raw[st][0].y, raw[st][0].z, raw[st][0].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wd[e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
+            } else {
+                const uint4 r1 = raw[st][BF16 ? 0 : 1];
+                wd[0] = pack_h2(__uint_as_float(raw[st][0].x), __uint_as_float(raw[st][0].y));
+                wd[1] = pack_h2(__uint_as_float(raw[st][0].z), __uint_as_float(raw[st][0].w));
+                wd[2] = pack_h2(__uint_as_float(r1.x), __uint_as_float(r1.y));
+                wd[3] = pack_h2(__uint_as_float(r1.z), __uint_as_float(r1.w));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wd[e] = hv ? wd[e] : 0u;
             qf[st] = __builtin_bit_cast(half8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
         }
     }
@@ -178,83 +202,123 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     int t_end = t_begin + a.tiles_per_split;
     if (t_end > a.n_tiles) t_end = a.n_tiles;
 
-    // dequant role of this thread: key group (step sg, group gg) = wave,
-    // 8-channel chunk j = lane
-    const int sg = wv >> 1, gg = wv & 1;
-    const int j = lane;
+    // index entries of the main-KV slots, staged kMaxTilesPerSplit tiles at
+    // a time (window starting at tile win0)
+    int win0 = t_begin;
+    auto stage_idx = [&](int first_tile) {
+        win0 = first_tile;
+        for (int i = tid; i < kMaxTilesPerSplit * kKT; i += NT) {
+            const int slot = first_tile * kKT + i;
+            idx_s[i] = slot < a.k ? idx[slot] : -1;
+        }
+    };
+    stage_idx(t_begin);
+    __syncthreads();
 
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        // ---------------- 1. gather + dequantise 32 rows
-        if (j < CH) {
-            uint32_t h[8][4];
+    // dequant role: this wave covers KPT keys of the 8-key group g8 (step
+    // sg = g8 >> 1, group gg = g8 & 1), slots i8 = i + 8 - ... of that group;
+    // lane j handles channels 8j..8j+7.
+    const int g8 = KPT == 8 ? wv : (wv >> 1);
+    const int half = KPT == 8 ? 0 : (wv & 1);
+    const int sg = g8 >> 1, gg = g8 & 1;
+    const int j = lane;
+    auto key_of_i = [&](int i) {
+        const int i8 = half * 4 + i;
+        return 16 * sg + 4 * gg + (i8 & 3) + 8 * (i8 >> 2);
+    };
+
+    // raw tile data for this thread's keys, prefetched one tile ahead:
+    // kind 0 empty, 1 MXFP4 row (code word + scale byte), 2 window row (16
+    // bytes of bf16 or 32 of float32).  Main and window rows use separate
+    // registers so a load never has to wait for another load's register.
+    constexpr int WWORDS = BF16 ? 4 : 8;
+    uint32_t raw_cw[KPT], raw_sc[KPT], raw_sw[KPT][WWORDS];
+    int raw_kind[KPT];
+    // Every branch below is wave-uniform (it depends on the key slot only);
+    // lanes past the row's chunk count load a clamped chunk and skip their
+    // stores later, so no load sits in a lane-divergent branch.
+    const int jl = j < CH ? j : 0;
+    auto load_raw = [&](int tile) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int key = 16 * sg + 4 * gg + (i & 3) + 8 * (i >> 2);
-                const int slot = tile * kKT + key;
-                bool valid = false;
-                if (slot < a.k) {
-                    const int32_t row = idx[slot];
-                    if (row >= 0 && row < a.cap) {
-                        valid = true;
-                        const int64_t rr = kvbase + row;
-                        const uint32_t cw = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * j);
-                        const uint32_t sc = a.scales[rr * (D / 16) + (j >> 1)] & 0x7fu;
-                        const uint32_t s16 = f16_bits(e4m3_val(sc));
-                        dequant8(cw, s16 | (s16 << 16), h[i]);
-                    }
-                } else if (slot < n_slots) {
-                    const int r = slot - a.k;
-                    if (r < n_swa) {
-                        valid = true;
-                        if (a.swa_bf16) {
-                            const uint4 v = *reinterpret_cast<const uint4*>(swa_rows + r * swa_row_bytes + 16 * j);
-                            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                h[i][e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
-                        } else {
-                            const float* f = reinterpret_cast<const float*>(swa_rows + r * swa_row_bytes) + 8 * j;
-                            const float4 x0 = *reinterpret_cast<const float4*>(f);
-                            const float4 x1 = *reinterpret_cast<const float4*>(f + 4);
-                            h[i][0] = pack_h2(x0.x, x0.y); h[i][1] = pack_h2(x0.z, x0.w);
-                            h[i][2] = pack_h2(x1.x, x1.y); h[i][3] = pack_h2(x1.z, x1.w);
-                        }
-                    }
+        for (int i = 0; i < KPT; ++i) {
+            const int slot = tile * kKT + key_of_i(i);
+            if (slot < a.k) {
+                const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * kKT]);
+                const bool ok = row >= 0 && row < a.cap;
+                const int64_t rr = kvbase + (ok ? row : 0);
+                raw_kind[i] = ok ? 1 : 0;
+                raw_cw[i] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * jl);
+                raw_sc[i] = a.scales[rr * (D / 16) + (jl >> 1)];
+            } else if (slot < n_slots && slot - a.k < n_swa) {
+                const int r = slot - a.k;
+                raw_kind[i] = 2;
+                const uint4* src = reinterpret_cast<const uint4*>(swa_rows + r * swa_row_bytes + WWORDS * 4 * jl);
+                const uint4 v0 = src[0];
+                raw_sw[i][0] = v0.x; raw_sw[i][1] = v0.y; raw_sw[i][2] = v0.z; raw_sw[i][3] = v0.w;
+                if (!BF16) {
+                    const uint4 v1 = src[1];
+                    raw_sw[i][WWORDS - 4] = v1.x; raw_sw[i][WWORDS - 3] = v1.y;
+                    raw_sw[i][WWORDS - 2] = v1.z; raw_sw[i][WWORDS - 1] = v1.w;
                 }
-                if (!valid) { h[i][0] = h[i][1] = h[i][2] = h[i][3] = 0u; }
-                if (j == 0) kvalid[key] = valid ? 1 : 0;
+            } else {
+                raw_kind[i] = 0;
+            }
+        }
+    };
+
+    // dequantise this thread's KPT keys (values in h) into Kt and Vt
+    auto store_tile = [&](const uint32_t (&h)[KPT][4], const int (&kind)[KPT]) {
+        if (j < CH) {
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const int key = key_of_i(i);
+                if (j == 0) kvalid[key] = kind[i] != 0 ? 1 : 0;
                 *reinterpret_cast<uint4*>(&Kt[key * KROW + 8 * j]) =
                     make_uint4(h[i][0], h[i][1], h[i][2], h[i][3]);
             }
-            // transpose 8 keys x 8 channels -> Vt[sg][gg][d][key i]
+            // transpose KPT keys x 8 channels into Vt[sg][gg][d][slot i8]
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                uint32_t lo4[4], hi4[4];
+                uint32_t lo4[KPT / 2], hi4[KPT / 2];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < KPT / 2; ++q) {
                     lo4[q] = __builtin_amdgcn_perm(h[2 * q + 1][p], h[2 * q][p], 0x05040100u);
                     hi4[q] = __builtin_amdgcn_perm(h[2 * q + 1][p], h[2 * q][p], 0x07060302u);
                 }
-                _Float16* base = &Vt[((sg * 2 + gg) * D + 8 * j + 2 * p) * 8];
-                *reinterpret_cast<uint4*>(base) = make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]);
-                *reinterpret_cast<uint4*>(base + 8) = make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]);
+                _Float16* base = &Vt[((sg * 2 + gg) * D + 8 * j + 2 * p) * 8 + 4 * half];
+                if (KPT == 8) {
+                    *reinterpret_cast<uint4*>(base) = make_uint4(lo4[0], lo4[1], lo4[KPT / 2 - 2], lo4[KPT / 2 - 1]);
+                    *reinterpret_cast<uint4*>(base + 8) = make_uint4(hi4[0], hi4[1], hi4[KPT / 2 - 2], hi4[KPT / 2 - 1]);
+                } else {
+                    *reinterpret_cast<uint2*>(base) = make_uint2(lo4[0], lo4[KPT / 2 - 1]);
+                    *reinterpret_cast<uint2*>(base + 8) = make_uint2(hi4[0], hi4[KPT / 2 - 1]);
+                }
             }
         }
-        __syncthreads();
+    };
 
-        // ---------------- 2. S^T partial over this wave's channel half
+    // S, online softmax and P.V for the tile currently in Kt/Vt
+    auto tile_math = [&]() {
+        // ---------------- 2. S^T partial over this wave's channel slice
         floatx16 s_acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_acc[r] = 0.0f;
 #pragma unroll
         for (int st = 0; st < SSTEPS; ++st) {
-            const int d0 = dh * DH + 16 * st + 8 * (lane >> 5);
+            const int d0 = dq * DQ + 16 * st + 8 * (lane >> 5);
             const half8 kf = *reinterpret_cast<const half8*>(&Kt[(lane & 31) * KROW + d0]);
             s_acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s_acc, 0, 0, 0);
         }
         int kv_ok[16];
+        {
+            const int4* kv4 = reinterpret_cast<const int4*>(kvalid);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) kv_ok[r] = kvalid[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
+            for (int r4 = 0; r4 < 4; ++r4) {
+                // rows 8*r4 + 4*(lane/32) + 0..3
+                const int4 v = kv4[2 * r4 + (lane >> 5)];
+                kv_ok[4 * r4] = v.x; kv_ok[4 * r4 + 1] = v.y; kv_ok[4 * r4 + 2] = v.z; kv_ok[4 * r4 + 3] = v.w;
+            }
+        }
         __syncthreads();   // everyone done reading Kt before Spart overwrites it
 #pragma unroll
         for (int r = 0; r < 16; ++r) Spart[(wv * 16 + r) * 64 + lane] = s_acc[r];
@@ -262,52 +326,144 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
         float t2[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float s = Spart[(hg * 16 + r) * 64 + lane] + Spart[((hg + 2) * 16 + r) * 64 + lane];
-            t2[r] = kv_ok[r] ? s * a.c2 : -__builtin_inff();
+            float sum = Spart[(hg * 16 + r) * 64 + lane];
+#pragma unroll
+            for (int qq = 1; qq < NQ; ++qq) sum += Spart[((hg + 2 * qq) * 16 + r) * 64 + lane];
+            t2[r] = kv_ok[r] ? sum * a.c2 : -__builtin_inff();
         }
 
-        // ---------------- 3. online softmax (base 2)
+        // ---------------- 3. online softmax (base 2) with a lazy reference:
+        // probabilities are exp2(t - m_ref); m_ref moves (and O, l are
+        // rescaled) only when some lane's tile max exceeds it by more than 8,
+        // so p stays below 2^8 and the rescale is rare.  The final division
+        // by l uses the same reference, so the result does not depend on it.
         float tmax = t2[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, t2[r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.0f;
+        const bool grow = tmax > m_run + 8.0f || (m_run == -__builtin_inff() && tmax != -__builtin_inff());
+        if (__ballot(grow) != 0) {
+            const float m_new = grow ? tmax : m_run;
+            const float alpha = (m_run == -__builtin_inff()) ? 0.0f : exp2f(m_run - m_new);
+            if (m_new != m_run) {
+                l_run *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o_acc[mt][r] *= alpha;
+            }
+            m_run = m_new;
+        }
         uint32_t pk[8];
         float psum = 0.0f;
-        if (m_new == -__builtin_inff()) {
+        if (m_run == -__builtin_inff()) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) pk[q] = 0u;
         } else {
-            alpha = exp2f(m_run - m_new);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const _Float16 p0 = static_cast<_Float16>(exp2f(t2[2 * q] - m_new));
-                const _Float16 p1 = static_cast<_Float16>(exp2f(t2[2 * q + 1] - m_new));
+                const _Float16 p0 = static_cast<_Float16>(exp2f(t2[2 * q] - m_run));
+                const _Float16 p1 = static_cast<_Float16>(exp2f(t2[2 * q + 1] - m_run));
                 psum += static_cast<float>(p0) + static_cast<float>(p1);
                 pk[q] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, p0)) |
                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, p1)) << 16);
             }
         }
-        m_run = m_new;
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o_acc[mt][r] *= alpha;
+        l_run += psum;
 
-        // ---------------- 4. O^T += V^T P^T
+        // ---------------- 4. O^T += V^T P^T over this wave's channel slice
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const half8 pf = __builtin_bit_cast(half8, make_uint4(pk[4 * ks], pk[4 * ks + 1],
                                                                   pk[4 * ks + 2], pk[4 * ks + 3]));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int d = dh * DH + 32 * mt + (lane & 31);
+                const int d = dq * DQ + 32 * mt + (lane & 31);
                 const half8 vf = *reinterpret_cast<const half8*>(&Vt[((ks * 2 + (lane >> 5)) * D + d) * 8]);
                 o_acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o_acc[mt], 0, 0, 0);
             }
         }
+    };
+
+    // ---- main tiles (every slot a main-KV slot): branch-free gathers
+    // prefetched one tile ahead into registers no other path writes
+    const int t_main_end = (a.k / kKT) < t_end ? (a.k / kKT) : t_end;
+    uint32_t pm_cw[KPT], pm_sc[KPT];
+    int pm_ok[KPT];
+    auto load_main = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int slot = tile * kKT + key_of_i(i);
+            const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * kKT]);
+            const bool ok = row >= 0 && row < a.cap;
+            const int64_t rr = kvbase + (ok ? row : 0);
+            pm_ok[i] = ok;
+            pm_cw[i] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * jl);
+            pm_sc[i] = a.scales[rr * (D / 16) + (jl >> 1)];
+        }
+    };
+    if (t_begin < t_main_end) load_main(t_begin);
+    for (int tile = t_begin; tile < t_main_end; ++tile) {
+        {
+            uint32_t h[KPT][4];
+            int kind[KPT];
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const uint32_t s16 = f16_bits(e4m3_val(pm_sc[i] & 0x7fu));
+                dequant8(pm_cw[i], s16 | (s16 << 16), h[i]);
+                kind[i] = pm_ok[i] ? 1 : 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[i][e] = pm_ok[i] ? h[i][e] : 0u;
+            }
+            store_tile(h, kind);
+        }
+        __syncthreads();
+        if (tile + 1 < t_main_end) {                // in flight during this tile's math
+            if (tile + 1 - win0 == kMaxTilesPerSplit) {
+                stage_idx(tile + 1);
+                __syncthreads();
+            }
+            load_main(tile + 1);
+        }
+        tile_math();
+        __syncthreads();
+    }
+
+    // ---- remaining tiles (window rows, or a tile straddling the main/window
+    // boundary): generic gather, not prefetched (at most a few tiles)
+    for (int tile = t_begin > t_main_end ? t_begin : t_main_end; tile < t_end; ++tile) {
+        if (tile - win0 >= kMaxTilesPerSplit) {
+            stage_idx(tile);
+            __syncthreads();
+        }
+        load_raw(tile);
+        {
+            uint32_t h[KPT][4];
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                if (raw_kind[i] == 1) {
+                    const uint32_t s16 = f16_bits(e4m3_val(raw_sc[i] & 0x7fu));
+                    dequant8(raw_cw[i], s16 | (s16 << 16), h[i]);
+                } else if (raw_kind[i] == 2) {
+                    if (BF16) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            h[i][e] = pack_h2(__uint_as_float(raw_sw[i][e] << 16),
+                                              __uint_as_float(raw_sw[i][e] & 0xffff0000u));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            h[i][e] = pack_h2(__uint_as_float(raw_sw[i][2 * e]),
+                                              __uint_as_float(raw_sw[i][2 * e + 1 < WWORDS ? 2 * e + 1 : 0]));
+                    }
+                } else {
+                    h[i][0] = h[i][1] = h[i][2] = h[i][3] = 0u;
+                }
+            }
+            store_tile(h, raw_kind);
+        }
+        __syncthreads();
+        tile_math();
         __syncthreads();
     }
 
@@ -323,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = dh * DH + 32 * mt + 8 * r4 + 4 * (lane >> 5);
+                    const int d = dq * DQ + 32 * mt + 8 * r4 + 4 * (lane >> 5);
                     *reinterpret_cast<float4*>(orow + d) =
                         make_float4(o_acc[mt][4 * r4] * inv, o_acc[mt][4 * r4 + 1] * inv,
                                     o_acc[mt][4 * r4 + 2] * inv, o_acc[mt][4 * r4 + 3] * inv);
@@ -336,37 +492,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) po[((wv * MT + mt) * 16 + r) * 64 + lane] = o_acc[mt][r];
-        if (dh == 0 && lane < 32) {
+        if (dq == 0 && lane < 32) {
             a.ws_m[pidx * 64 + head_local] = m_run;
             a.ws_l[pidx * 64 + head_local] = l_tot;
         }
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ws_o,
-                                                      const float* __restrict__ ws_m,
-                                                      const float* __restrict__ ws_l, int splits,
-                                                      int H, int hblocks, float* __restrict__ out) {
-    constexpr int DH = D / 2, MT = DH / 32;
+// Merge the key-split partials of one (unit, 64-head block): workgroup y
+// covers one (wave, row-tile) block of the partial layout, i.e. 32 heads x
+// 32 consecutive channels.  Reads are in the partials' own (coalesced)
+// order; the result is transposed through LDS so the output rows are
+// written as 128-byte runs.
+template <int D, int NQ>
+__global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ ws_o,
+                                                       const float* __restrict__ ws_m,
+                                                       const float* __restrict__ ws_l, int splits,
+                                                       int H, int hblocks, float* __restrict__ out) {
+    constexpr int DQ = D / NQ, MT = DQ / 32;
+    __shared__ float tile[32][33];
     const int64_t ub = blockIdx.x;                 // unit * hblocks + hb
-    const int e = blockIdx.y * 256 + threadIdx.x;  // head_local * D + d
-    if (e >= 64 * D) return;
-    const int head_local = e / D, d = e % D;
-    const int hb = static_cast<int>(ub % hblocks);
-    const int64_t u = ub / hblocks;
-    const int head = hb * 64 + head_local;
-    if (head >= H) return;
-    const int hg = head_local / 32, dhh = d / DH, dd = d % DH;
-    const int mt = dd / 32, x = dd % 32;
-    const int r = 4 * (x / 8) + (x % 4);
-    const int ln = 32 * ((x % 8) / 4) + (head_local % 32);
-    const int wv = hg + 2 * dhh;
+    const int wv = blockIdx.y / MT, mt = blockIdx.y % MT;
+    const int hg = wv & 1, dqq = wv >> 1;
+    const int t = threadIdx.x, r = t >> 6, ln = t & 63;
+    const int head_local = 32 * hg + (ln & 31);
+    const int dd = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
     const int64_t nat = ((wv * MT + mt) * 16 + r) * 64 + ln;
     float mstar = -__builtin_inff();
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, ws_m[(ub * splits + s) * 64 + head_local]);
     float num = 0.0f, den = 0.0f;
     if (mstar != -__builtin_inff()) {
+#pragma unroll 8
         for (int s = 0; s < splits; ++s) {
             const int64_t p = ub * splits + s;
             const float ms = ws_m[p * 64 + head_local];
@@ -376,7 +533,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             den += wgt * ws_l[p * 64 + head_local];
         }
     }
-    out[(u * H + head) * D + d] = den > 0.0f ? num / den : 0.0f;
+    tile[ln & 31][dd] = den > 0.0f ? num / den : 0.0f;
+    __syncthreads();
+    const int hb = static_cast<int>(ub % hblocks);
+    const int64_t u = ub / hblocks;
+    const int oh = t >> 5, od = t & 31;
+    const int head = hb * 64 + 32 * hg + oh;
+    if (head < H) out[(u * H + head) * D + dqq * DQ + 32 * mt + od] = tile[oh][od];
 }
 
 struct SplitPlan { int splits, tiles_per_split, n_tiles; };
@@ -397,7 +560,7 @@ SplitPlan plan(int64_t units, int H, int k, int W) {
     return p;
 }
 
-template <int D>
+template <int D, int NQ, bool BF16>
 hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     const SplitPlan sp = plan(L.units, L.H, L.k, L.W);
     const int hblocks = (L.H + 63) / 64;
@@ -414,10 +577,10 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     a.ws_m = L.ws ? L.ws + nparts * 64 * D : nullptr;
     a.ws_l = L.ws ? a.ws_m + nparts * 64 : nullptr;
     if (L.units == 0) return hipSuccess;
-    attn_kernel<D><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), kThreads, 0, st>>>(a);
+    attn_kernel<D, NQ, BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 128 * NQ, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sp.splits == 1) return e;
-    combine_kernel<D><<<dim3(static_cast<unsigned>(L.units * hblocks), (64 * D + 255) / 256), 256, 0, st>>>(
+    combine_kernel<D, NQ><<<dim3(static_cast<unsigned>(L.units * hblocks), 2 * NQ * (D / NQ / 32)), 1024, 0, st>>>(
         a.ws_o, a.ws_m, a.ws_l, sp.splits, L.H, hblocks, L.out);
     return hipGetLastError();
 }
@@ -437,8 +600,9 @@ size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W) {
 }
 
 hipError_t launch_attn(const AttnLaunch& L, hipStream_t st) {
-    if (L.D == 512) return launch_d<512>(L, st);
-    if (L.D == 64) return launch_d<64>(L, st);
+    if (L.q_bf16 != L.swa_bf16) return hipErrorInvalidValue;
+    if (L.D == 512) return L.q_bf16 ? launch_d<512, 4, true>(L, st) : launch_d<512, 4, false>(L, st);
+    if (L.D == 64) return L.q_bf16 ? launch_d<64, 2, true>(L, st) : launch_d<64, 2, false>(L, st);
     return hipErrorInvalidValue;
 }
 

@@ -65,18 +65,14 @@ int mxfp4_kv_write(const void* x, int x_dtype, int64_t n_rows, int32_t D, const 
         if (!idx_k_cache) return fail(CSA2_E_INVALID, "mxfp4_kv_write: idx_k_cache is null");
         if (!valid_dtype(idx_k_dtype)) return fail(CSA2_E_INVALID, "mxfp4_kv_write: bad idx_k_dtype");
         const int64_t rb = static_cast<int64_t>(d_I) * static_cast<int64_t>(dtype_size(idx_k_dtype));
-        if (d_I <= 0 || rb % 4 != 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: indexer row bytes must be a positive multiple of 4");
-        if (!aligned(idx_k_rows, 4) || !aligned(idx_k_cache, 4))
-            return fail(CSA2_E_INVALID, "mxfp4_kv_write: indexer rows must be 4-byte aligned");
+        if (d_I <= 0 || rb % 16 != 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: indexer row bytes must be a positive multiple of 16");
+        if (n_cache_rows % 64 != 0) return fail(CSA2_E_INVALID, "mxfp4_kv_write: the tiled indexer cache needs n_cache_rows %% 64 == 0");
+        if (!aligned(idx_k_rows, 16) || !aligned(idx_k_cache, 16))
+            return fail(CSA2_E_INVALID, "mxfp4_kv_write: indexer rows must be 16-byte aligned");
     }
-    hipError_t e = csa2::launch_kv_quantize(x, x_dtype == CSA2_BF16, n_rows, D, dst_row, n_cache_rows,
-                                            codes, scales, as_stream(stream));
-    if (e != hipSuccess) return device_status(e, "mxfp4_kv_write");
-    if (idx_k_rows) {
-        const int64_t rb = static_cast<int64_t>(d_I) * static_cast<int64_t>(dtype_size(idx_k_dtype));
-        e = csa2::launch_row_copy(idx_k_rows, n_rows, rb, dst_row, n_cache_rows, idx_k_cache,
-                                  as_stream(stream));
-    }
+    const int64_t rb = idx_k_rows ? static_cast<int64_t>(d_I) * static_cast<int64_t>(dtype_size(idx_k_dtype)) : 0;
+    hipError_t e = csa2::launch_kv_write(x, x_dtype == CSA2_BF16, n_rows, D, dst_row, n_cache_rows, codes,
+                                         scales, idx_k_rows, rb, idx_k_cache, as_stream(stream));
     return device_status(e, "mxfp4_kv_write");
 }
 
@@ -98,6 +94,7 @@ static int check_score_args(const csa2_score_args* a) {
             return fail(CSA2_E_INVALID, "csa2_index_score: ld_scores must be >= 8*P_b in pool mode");
         if (a->block_max) return fail(CSA2_E_INVALID, "csa2_index_score: block_max is for Full mode only");
     }
+    if (a->cap % 64 != 0) return fail(CSA2_E_INVALID, "csa2_index_score: cap must be a multiple of 64 (tiled indexer cache)");
     if (a->B * a->Tq == 0) return CSA2_OK;
     if (!a->q_idx || !a->w || !a->k_idx || !a->ctx_len || !a->scores)
         return fail(CSA2_E_INVALID, "csa2_index_score: null pointer");
@@ -106,20 +103,15 @@ static int check_score_args(const csa2_score_args* a) {
 }
 
 size_t csa2_index_score_workspace_size(const csa2_score_args* a) {
-    if (!a || a->B < 0 || a->Tq < 0 || a->H_I <= 0 || a->d_I <= 0) return 0;
-    const size_t bytes = static_cast<size_t>(a->B * a->Tq) * static_cast<size_t>(a->H_I) *
-                         static_cast<size_t>(a->d_I) * sizeof(float);
-    return (bytes + 255) / 256 * 256;
+    (void)a;
+    return 0;
 }
 
 int csa2_index_score(const csa2_score_args* a, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_score_args(a);
     if (rc != CSA2_OK) return rc;
     if (a->B * a->Tq == 0 || a->ld_scores == 0) return ok();
-    const size_t need = csa2_index_score_workspace_size(a);
-    if (!ws || ws_bytes < need)
-        return fail(CSA2_E_WORKSPACE, "csa2_index_score: workspace %zu bytes < required %zu", ws_bytes, need);
-    if (!aligned(ws, 16)) return fail(CSA2_E_INVALID, "csa2_index_score: workspace must be 16-byte aligned");
+    (void)ws; (void)ws_bytes;
     csa2::ScoreLaunch p;
     p.q_idx = a->q_idx; p.q_bf16 = a->q_dtype == CSA2_BF16;
     p.w = a->w; p.k_idx = a->k_idx; p.k_bf16 = a->k_dtype == CSA2_BF16;
@@ -128,20 +120,19 @@ int csa2_index_score(const csa2_score_args* a, void* ws, size_t ws_bytes, void* 
     p.pool = a->pool_blocks; p.P_b = a->pool_blocks ? a->P_b : 0;
     p.scores = a->scores; p.ld = a->ld_scores;
     p.block_max = a->block_max; p.ld_bm = (a->ld_scores + 7) / 8;
-    p.qT = static_cast<float*>(ws);
     return device_status(csa2::launch_score(p, as_stream(stream)), "csa2_index_score");
 }
 
 // --------------------------------------------------------------------------
 size_t csa2_topk_workspace_size(int64_t rows, int64_t n, int32_t k) {
-    (void)rows; (void)n; (void)k;
-    return 0;
+    (void)k;
+    if (rows <= 0 || n <= 0) return 0;
+    return csa2::topk_workspace_bytes(rows, n);
 }
 
 int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int32_t k,
               const int32_t* pool_blocks, int32_t P_b, int32_t* out_idx, void* ws, size_t ws_bytes,
               void* stream) {
-    (void)ws; (void)ws_bytes;
     if (rows < 0 || n < 0 || ld < n) return fail(CSA2_E_INVALID, "csa2_topk: need rows >= 0 and 0 <= n <= ld");
     if (k <= 0) return fail(CSA2_E_INVALID, "csa2_topk: k must be positive");
     if (n > (int64_t(1) << 31) - 1) return fail(CSA2_E_UNSUPPORTED, "csa2_topk: n above 2^31-1");
@@ -149,23 +140,48 @@ int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int32_t 
         return fail(CSA2_E_INVALID, "csa2_topk: with pool_blocks, n must equal 8*P_b");
     if (rows == 0) return ok();
     if (!scores || !out_idx) return fail(CSA2_E_INVALID, "csa2_topk: null pointer");
-    return device_status(csa2::launch_topk(scores, rows, n, ld, k, pool_blocks, P_b, out_idx, as_stream(stream)),
+    const size_t need = csa2_topk_workspace_size(rows, n, k);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(CSA2_E_WORKSPACE, "csa2_topk: workspace %zu bytes < required %zu", ws_bytes, need);
+    if (need > 0 && !aligned(ws, 256)) return fail(CSA2_E_INVALID, "csa2_topk: workspace must be 256-byte aligned");
+    return device_status(csa2::launch_topk(scores, rows, n, ld, k, pool_blocks, P_b, out_idx, ws, as_stream(stream)),
                          "csa2_topk");
 }
 
 size_t csa2_build_candidate_pool_workspace_size(int64_t rows, int64_t n_blocks, int32_t P_b) {
+    if (csa2::pool_in_lds(n_blocks, P_b)) return 0;
     return csa2_topk_workspace_size(rows, n_blocks, P_b);
 }
 
 int csa2_build_candidate_pool(const float* block_max, int64_t rows, int64_t n_blocks, int64_t ld,
                               int32_t P_b, int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream) {
     if (P_b <= 0) return fail(CSA2_E_INVALID, "csa2_build_candidate_pool: P_b must be positive");
+    if (rows < 0 || n_blocks < 0 || ld < n_blocks)
+        return fail(CSA2_E_INVALID, "csa2_build_candidate_pool: need rows >= 0 and 0 <= n_blocks <= ld");
+    if (rows == 0) return ok();
+    if (!block_max || !out_blocks) return fail(CSA2_E_INVALID, "csa2_build_candidate_pool: null pointer");
+    if (csa2::pool_in_lds(n_blocks, P_b))
+        return device_status(csa2::launch_pool(block_max, rows, n_blocks, ld, P_b, out_blocks, as_stream(stream)),
+                             "csa2_build_candidate_pool");
     int rc = csa2_topk(block_max, rows, n_blocks, ld, P_b, nullptr, 0, out_blocks, ws, ws_bytes, stream);
     if (rc != CSA2_OK) {
         std::string m = "csa2_build_candidate_pool: " + g_last_error;
         g_last_error = m;
     }
     return rc;
+}
+
+int csa2_topk_from_pool(const float* scores, int64_t rows, int64_t ld, const int32_t* pool_blocks, int32_t P_b,
+                        int32_t k, int32_t* out_idx, void* stream) {
+    if (rows < 0 || ld < 0) return fail(CSA2_E_INVALID, "csa2_topk_from_pool: negative size");
+    if (k <= 0 || P_b <= 0 || k > P_b)
+        return fail(CSA2_E_INVALID, "csa2_topk_from_pool: need 0 < k <= P_b (the pool holds the top-k only then)");
+    if (static_cast<int64_t>(P_b) * 8 > 32768)
+        return fail(CSA2_E_UNSUPPORTED, "csa2_topk_from_pool: 8*P_b above 32768");
+    if (rows == 0) return ok();
+    if (!scores || !pool_blocks || !out_idx) return fail(CSA2_E_INVALID, "csa2_topk_from_pool: null pointer");
+    return device_status(csa2::launch_topk_from_pool(scores, rows, ld, pool_blocks, P_b, k, out_idx, as_stream(stream)),
+                         "csa2_topk_from_pool");
 }
 
 // --------------------------------------------------------------------------
@@ -176,10 +192,12 @@ static int check_attn_common(const char* fn, const void* q, int q_dtype, const u
     if (units < 0 || cap < 0) return fail(CSA2_E_INVALID, "%s: negative size", fn);
     if (k < 0 || W < 0 || k + W <= 0) return fail(CSA2_E_INVALID, "%s: need k >= 0, W >= 0, k + W > 0", fn);
     if (!valid_dtype(q_dtype) || !valid_dtype(swa_dtype)) return fail(CSA2_E_INVALID, "%s: bad dtype", fn);
+    if (q_dtype != swa_dtype) return fail(CSA2_E_UNSUPPORTED, "%s: q and swa must share a dtype", fn);
     if (H <= 0 || D <= 0 || D % 16 != 0) return fail(CSA2_E_INVALID, "%s: bad H=%d or D=%d", fn, H, D);
     if (!csa2::attn_shape_supported(H, D))
         return fail(CSA2_E_UNSUPPORTED, "%s: (H=%d, D=%d) not instantiated (D=512 with H %% 64 == 0, or D=64 with H <= 64)",
                     fn, H, D);
+    if (k > 0 && cap <= 0) return fail(CSA2_E_INVALID, "%s: k > 0 needs a non-empty cache (cap >= 1)", fn);
     if (units == 0) return CSA2_OK;
     if (!q || !out || (k > 0 && (!codes || !scales || !idx)) || (W > 0 && !swa))
         return fail(CSA2_E_INVALID, "%s: null pointer", fn);

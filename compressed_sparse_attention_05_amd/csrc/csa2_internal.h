@@ -9,12 +9,11 @@ namespace csa2 {
 
 // Launchers: return hipSuccess or the launch error.  Arguments are already
 // validated by the entry points in csa2_api.hip.
-hipError_t launch_kv_quantize(const void* x, bool x_bf16, int64_t n_rows, int D,
-                              const int64_t* dst_row, int64_t n_cache_rows, uint8_t* codes,
-                              uint8_t* scales, hipStream_t st);
-hipError_t launch_row_copy(const void* src, int64_t n_rows, int64_t row_bytes,
-                           const int64_t* dst_row, int64_t n_cache_rows, void* dst,
-                           hipStream_t st);
+// MXFP4 quantisation of n_rows rows plus (krows != NULL) the copy of their
+// indexer-K rows (krow_bytes each) into the tiled indexer cache.
+hipError_t launch_kv_write(const void* x, bool x_bf16, int64_t n_rows, int D, const int64_t* dst_row,
+                           int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const void* krows,
+                           int64_t krow_bytes, void* kcache, hipStream_t st);
 
 struct ScoreLaunch {
     const void* q_idx; bool q_bf16;
@@ -28,13 +27,20 @@ struct ScoreLaunch {
     const int32_t* pool; int P_b;
     float* scores; int64_t ld;
     float* block_max; int64_t ld_bm;
-    float* qT;   // workspace [B*Tq][d_I][H_I] float32
 };
 bool score_shape_supported(int H_I, int d_I);
 hipError_t launch_score(const ScoreLaunch& p, hipStream_t st);
 
+size_t topk_workspace_bytes(int64_t rows, int64_t n);
+// Full-mode top-k gathered through a candidate pool (k <= P_b, 8*P_b <= 32768).
+hipError_t launch_topk_from_pool(const float* scores, int64_t rows, int64_t ld, const int32_t* pool, int P_b,
+                                 int k, int32_t* out, hipStream_t st);
+// Pool selection staged in LDS (directly, or through super-blocks of 8 blocks).
+bool pool_in_lds(int64_t n_blocks, int P_b);
+hipError_t launch_pool(const float* bmax, int64_t rows, int64_t n_blocks, int64_t ld, int P_b, int32_t* out,
+                       hipStream_t st);
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int k,
-                       const int32_t* pool, int P_b, int32_t* out, hipStream_t st);
+                       const int32_t* pool, int P_b, int32_t* out, void* ws, hipStream_t st);
 
 struct AttnLaunch {
     const void* q; bool q_bf16;

@@ -8,8 +8,9 @@
 // exact float32 comparison against a threshold that float32 holds exactly,
 // so the bytes are reproducible on any device.
 //
-// One thread per (row, 16-channel block): the work is a few hundred bytes per
-// decode token, so the kernel is launch-bound and kept plain.
+// One thread per (row, 16-channel block), plus one per 16-byte chunk of the
+// indexer-K rows: the work is a few hundred bytes per decode token, so the
+// kernel is launch-bound and does both jobs in one launch.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -48,13 +49,27 @@ __device__ __forceinline__ uint32_t mag_code(float a, float s) {
     return c;
 }
 
+// Threads [0, n_rows*D/16) quantise one 16-channel block each; the next
+// n_rows*nch threads copy one 16-byte chunk of an indexer-K row each into the
+// tiled indexer cache (chunk c of flat row r at ((r/64)*nch + c)*64 + r%64,
+// in 16-byte units).  One launch per write.
 template <bool BF16>
-__global__ __launch_bounds__(256) void kv_quantize_kernel(
+__global__ __launch_bounds__(256) void kv_write_kernel(
     const void* __restrict__ x, int64_t n_rows, int D, const int64_t* __restrict__ dst_row,
-    int64_t n_cache_rows, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    int64_t n_cache_rows, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    const uint4* __restrict__ krows, int nch, uint4* __restrict__ kcache) {
     const int nblk = D / 16;
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gid >= n_rows * nblk) return;
+    int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= n_rows * nblk) {
+        gid -= n_rows * nblk;
+        if (gid >= n_rows * nch) return;
+        const int64_t row = gid / nch;
+        const int c = static_cast<int>(gid % nch);
+        const int64_t r = dst_row[row];
+        if (r < 0 || r >= n_cache_rows) return;
+        kcache[((r >> 6) * nch + c) * 64 + (r & 63)] = krows[row * nch + c];
+        return;
+    }
     const int64_t row = gid / nblk;
     const int blk = static_cast<int>(gid % nblk);
     const int64_t dst = dst_row[row];
@@ -99,41 +114,21 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(
     scales[dst * nblk + blk] = static_cast<uint8_t>(sc);
 }
 
-__global__ __launch_bounds__(256) void row_copy_kernel(
-    const uint32_t* __restrict__ src, int64_t n_rows, int64_t row_words,
-    const int64_t* __restrict__ dst_row, int64_t n_cache_rows, uint32_t* __restrict__ dst) {
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gid >= n_rows * row_words) return;
-    const int64_t row = gid / row_words, wd = gid % row_words;
-    const int64_t d = dst_row[row];
-    if (d < 0 || d >= n_cache_rows) return;
-    dst[d * row_words + wd] = src[row * row_words + wd];
-}
-
 }  // namespace
 
-hipError_t launch_kv_quantize(const void* x, bool x_bf16, int64_t n_rows, int D,
-                              const int64_t* dst_row, int64_t n_cache_rows, uint8_t* codes,
-                              uint8_t* scales, hipStream_t st) {
-    const int64_t n = n_rows * (D / 16);
+hipError_t launch_kv_write(const void* x, bool x_bf16, int64_t n_rows, int D, const int64_t* dst_row,
+                           int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const void* krows,
+                           int64_t krow_bytes, void* kcache, hipStream_t st) {
+    const int nch = krows ? static_cast<int>(krow_bytes / 16) : 0;
+    const int64_t n = n_rows * (D / 16) + n_rows * nch;
     if (n == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+    const uint4* kr = static_cast<const uint4*>(krows);
+    uint4* kc = static_cast<uint4*>(kcache);
     if (x_bf16)
-        kv_quantize_kernel<true><<<grid, 256, 0, st>>>(x, n_rows, D, dst_row, n_cache_rows, codes, scales);
+        kv_write_kernel<true><<<grid, 256, 0, st>>>(x, n_rows, D, dst_row, n_cache_rows, codes, scales, kr, nch, kc);
     else
-        kv_quantize_kernel<false><<<grid, 256, 0, st>>>(x, n_rows, D, dst_row, n_cache_rows, codes, scales);
-    return hipGetLastError();
-}
-
-hipError_t launch_row_copy(const void* src, int64_t n_rows, int64_t row_bytes,
-                           const int64_t* dst_row, int64_t n_cache_rows, void* dst,
-                           hipStream_t st) {
-    const int64_t words = row_bytes / 4;
-    const int64_t n = n_rows * words;
-    if (n == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-    row_copy_kernel<<<grid, 256, 0, st>>>(static_cast<const uint32_t*>(src), n_rows, words, dst_row,
-                                          n_cache_rows, static_cast<uint32_t*>(dst));
+        kv_write_kernel<false><<<grid, 256, 0, st>>>(x, n_rows, D, dst_row, n_cache_rows, codes, scales, kr, nch, kc);
     return hipGetLastError();
 }
 

@@ -6,65 +6,81 @@
 //     d_h = fma chain over channels c = 0..d_I-1 of q[h][c] * k[c]
 //     s   = fma chain over heads h = 0..H_I-1 of w[h] * max(d_h, +0)
 // in float32, exactly in this order, so every score is bit-reproducible and
-// the top-k that follows is exact.
+// the top-k that follows is exact.  The chain forces one lane per (position,
+// head) to walk all channels in order, so each lane owns whole key rows.
 //
-// Design (HBM-bound stream, VALU co-limited):
-//  * one thread owns one position (one key row) and computes all H_I chains,
-//    so each widened key value feeds H_I fmas and the bf16->f32 widening
-//    costs one op per channel;
-//  * the query is pre-transposed to [d_I][H_I] float32 so a channel's H_I
-//    weights are one uniform 32-byte scalar load (SGPR operands of v_fma);
-//  * key rows are streamed with coalesced 16-byte loads into registers one
-//    256-row tile ahead, then stored to LDS with a 16-byte-chunk XOR swizzle
-//    (chunk c of row r at c ^ (r % chunks)) so the per-thread row reads are
-//    bank-conflict free;
-//  * the block max over 8 positions (candidate-pool input, notes section 3)
+// Design (HBM stream, VALU co-limited at ~1,180 VALU ops per 256-byte row):
+//  * The indexer-K cache is stored tiled (64 positions per tile, 16-byte
+//    chunks chunk-major: chunk c of position p of tile t at
+//    ((t * NCH + c) * 64 + p) * 16).  A wave reading chunk c of its 64
+//    positions reads 1 KiB of contiguous memory, and every lane receives its
+//    own row's chunk directly in registers: no LDS staging, no barriers.
+//  * Each lane owns two positions (two tiles), so every broadcast query value
+//    feeds two fmas and the bf16 -> f32 widening costs one op per channel.
+//  * The query, transposed to [d_I][H_I] float32, sits in LDS and is read
+//    with same-address (broadcast) 16-byte reads; LDS completions are in
+//    order, so reads for the next channel overlap the current fmas.
+//  * The block max over 8 positions (candidate-pool input, notes section 3)
 //    is fused: 8 consecutive lanes own one block.
 #include "csa2_internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kTile = 256;   // positions per tile = threads per workgroup
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnit = 128;          // positions per wave iteration (2 tiles of 64)
 
 struct ScoreArgs {
-    const float* qT;    // [rows][d_I][H_I]
-    const float* w;     // [rows][H_I]
-    const uint8_t* k;   // [B][cap][d_I] raw bytes
     int64_t cap, Tq;
     const int32_t* ctx_len;
     const int64_t* q_pos;
     int m;
     const int32_t* pool; int P_b;
-    float* scores; int64_t ld;
-    float* block_max; int64_t ld_bm;
-    int64_t n_slots;      // slots written per row
-    int64_t tiles_per_row;
-    int tiles_per_wg;
+    int64_t ld, ld_bm;
+    int64_t n_slots;          // slots written per row
+    int64_t units_per_row;    // ceil(n_slots / kUnit)
+    int units_per_wg;
+    int q_bf16;
 };
 
 template <int HI, int DI, bool KBF16>
-__global__ __launch_bounds__(kTile) void score_kernel(const float* __restrict__ qT_all,
-                                                      const float* __restrict__ w_all,
-                                                      const uint8_t* __restrict__ k_all,
-                                                      float* __restrict__ scores,
-                                                      float* __restrict__ block_max,
-                                                      ScoreArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(const void* __restrict__ q_all,
+                                                         const float* __restrict__ w_all,
+                                                         const uint8_t* __restrict__ k_all,
+                                                         float* __restrict__ scores,
+                                                         float* __restrict__ block_max,
+                                                         ScoreArgs a) {
     constexpr int ESZ = KBF16 ? 2 : 4;
     constexpr int ROWB = DI * ESZ;        // bytes per key row
     constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
     constexpr int CPC = 16 / ESZ;         // channels per chunk
-    constexpr int ROWS_PER_PASS = kTile / NCH;
-    __shared__ uint4 tile[kTile * NCH];
+    constexpr int G = NCH >= 4 ? 4 : NCH;  // chunks per streamed group
+    static_assert(NCH % G == 0, "chunk groups must tile the row");
+    static_assert(HI % 4 == 0 || HI == 2, "head count must be 2 or a multiple of 4");
+    __shared__ __attribute__((aligned(16))) float qs[DI * HI];   // [c][h]
 
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t row = blockIdx.y;       // query row (b * Tq + tq)
     const int64_t b = row / a.Tq;
-    const float* qT = qT_all + row * (DI * HI);
-    const float* w = w_all + row * HI;
-    const uint8_t* kb = k_all + b * a.cap * ROWB;
-    const int32_t* __restrict__ pool = a.pool ? a.pool + row * a.P_b : nullptr;
 
+    // query -> LDS, transposed to [c][h], widened to float32
+    for (int i = t; i < HI * DI; i += kThreads) {
+        const int h = i / DI, c = i % DI;
+        float v;
+        if (a.q_bf16)
+            v = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q_all)[row * HI * DI + i]) << 16);
+        else
+            v = static_cast<const float*>(q_all)[row * HI * DI + i];
+        qs[c * HI + h] = v;
+    }
+    float wh[HI];
+#pragma unroll
+    for (int h = 0; h < HI; ++h) wh[h] = w_all[row * HI + h];
+    __syncthreads();
+
+    const uint8_t* kb = k_all + b * a.cap * ROWB;        // cap is a multiple of 64
+    const int32_t* pool = a.pool ? a.pool + row * a.P_b : nullptr;
     int64_t vis = a.ctx_len[b];
     if (a.q_pos) {
         const int64_t v2 = (a.q_pos[row] + 1) / a.m;
@@ -83,122 +99,130 @@ __global__ __launch_bounds__(kTile) void score_kernel(const float* __restrict__ 
         return pos < vis ? pos : -1;
     };
 
-    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * a.tiles_per_wg;
-    int64_t tile1 = tile0 + a.tiles_per_wg;
-    if (tile1 > a.tiles_per_row) tile1 = a.tiles_per_row;
+    const int64_t u0 = static_cast<int64_t>(blockIdx.x) * a.units_per_wg;
+    int64_t u1 = u0 + a.units_per_wg;
+    if (u1 > a.units_per_row) u1 = a.units_per_row;
 
-    uint4 stage[NCH];
-    auto load_tile = [&](int64_t tl) {
-        const int64_t base = tl * kTile;
+    for (int64_t u = u0 + wv; u < u1; u += kWaves) {
+        int64_t slot[2], pos[2];
+        const uint8_t* base[2];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int r = i * ROWS_PER_PASS + t / NCH;
-            const int c = t % NCH;
-            const int64_t pos = pos_of(base + r);
-            if (pos >= 0)
-                stage[i] = *reinterpret_cast<const uint4*>(kb + pos * ROWB + c * 16);
-            else
-                stage[i] = make_uint4(0, 0, 0, 0);
+        for (int p = 0; p < 2; ++p) {
+            slot[p] = u * kUnit + p * 64 + lane;
+            pos[p] = pos_of(slot[p]);
+            const int64_t pp = pos[p] < 0 ? 0 : pos[p];
+            base[p] = kb + ((pp >> 6) * NCH * 64 + (pp & 63)) * 16;
         }
-    };
-
-    if (tile0 < tile1) load_tile(tile0);
-    for (int64_t tl = tile0; tl < tile1; ++tl) {
+        // Stream the row chunks in groups of G (registers hold the current
+        // group and the next one in flight); the group loop is not unrolled
+        // so the compiler cannot hoist every load and query read at once.
+        uint4 cur[2][G];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int r = i * ROWS_PER_PASS + t / NCH;
-            const int c = t % NCH;
-            tile[r * NCH + (c ^ (r % NCH))] = stage[i];
-        }
-        __syncthreads();
-        if (tl + 1 < tile1) load_tile(tl + 1);
-
-        const int64_t slot = tl * kTile + t;
-        const int64_t pos = pos_of(slot);
-        float acc[HI];
+        for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int h = 0; h < HI; ++h) acc[h] = 0.0f;
+            for (int p = 0; p < 2; ++p)
+                cur[p][j] = pos[p] >= 0 ? *reinterpret_cast<const uint4*>(base[p] + j * 1024)
+                                        : make_uint4(0, 0, 0, 0);
+        float acc[2][HI];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const uint4 v = tile[t * NCH + (c ^ (t % NCH))];
-            float kv[CPC];
-            if (KBF16) {
-                const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kv[2 * e] = __uint_as_float(wd[e] << 16);
-                    kv[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+            for (int h = 0; h < HI; ++h) acc[p][h] = 0.0f;
+#pragma unroll 1
+        for (int g = 0; g < NCH / G; ++g) {
+            uint4 nxt[2][G];
+            const bool more = g + 1 < NCH / G;
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    nxt[p][j] = (more && pos[p] >= 0)
+                                    ? *reinterpret_cast<const uint4*>(base[p] + ((g + 1) * G + j) * 1024)
+                                    : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int c = g * G + j;
+                float kv[2][CPC];
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    if (KBF16) {
+                        const uint32_t wd[4] = {cur[p][j].x, cur[p][j].y, cur[p][j].z, cur[p][j].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            kv[p][2 * e] = __uint_as_float(wd[e] << 16);
+                            kv[p][2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+                        }
+                    } else {
+                        kv[p][0] = __uint_as_float(cur[p][j].x); kv[p][1] = __uint_as_float(cur[p][j].y);
+                        kv[p][2] = __uint_as_float(cur[p][j].z); kv[p][3] = __uint_as_float(cur[p][j].w);
+                    }
                 }
-            } else {
-                kv[0] = __uint_as_float(v.x); kv[1] = __uint_as_float(v.y);
-                kv[2] = __uint_as_float(v.z); kv[3] = __uint_as_float(v.w);
+#pragma unroll
+                for (int e = 0; e < CPC; ++e) {
+                    const int ch = c * CPC + e;
+                    float qv[HI];
+                    if (HI % 4 == 0) {
+#pragma unroll
+                        for (int h4 = 0; h4 < HI / 4; ++h4) {
+                            const float4 q4 = *reinterpret_cast<const float4*>(&qs[ch * HI + 4 * h4]);
+                            qv[4 * h4] = q4.x; qv[4 * h4 + 1] = q4.y; qv[4 * h4 + 2] = q4.z; qv[4 * h4 + 3] = q4.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < HI; ++h) qv[h] = qs[ch * HI + h];
+                    }
+#pragma unroll
+                    for (int h = 0; h < HI; ++h) {
+                        acc[0][h] = __builtin_fmaf(qv[h], kv[0][e], acc[0][h]);
+                        acc[1][h] = __builtin_fmaf(qv[h], kv[1][e], acc[1][h]);
+                    }
+                }
             }
 #pragma unroll
-            for (int e = 0; e < CPC; ++e) {
-                const int ch = c * CPC + e;
+            for (int j = 0; j < G; ++j)
 #pragma unroll
-                for (int h = 0; h < HI; ++h) acc[h] = __builtin_fmaf(qT[ch * HI + h], kv[e], acc[h]);
+                for (int p = 0; p < 2; ++p) cur[p][j] = nxt[p][j];
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float s = 0.0f;
+#pragma unroll
+            for (int h = 0; h < HI; ++h) s = __builtin_fmaf(wh[h], acc[p][h] > 0.0f ? acc[p][h] : 0.0f, s);
+            if (pos[p] < 0) s = -__builtin_inff();
+            if (slot[p] < a.n_slots) scores[row * a.ld + slot[p]] = s;
+            if (block_max) {
+                float mx = s;
+                mx = fmaxf(mx, __shfl_xor(mx, 1));
+                mx = fmaxf(mx, __shfl_xor(mx, 2));
+                mx = fmaxf(mx, __shfl_xor(mx, 4));
+                if (mx == 0.0f) mx = 0.0f;
+                const int64_t blk = slot[p] >> 3;
+                if ((lane & 7) == 0 && blk < a.ld_bm) block_max[row * a.ld_bm + blk] = mx;
             }
         }
-        float s = 0.0f;
-#pragma unroll
-        for (int h = 0; h < HI; ++h) s = __builtin_fmaf(w[h], acc[h] > 0.0f ? acc[h] : 0.0f, s);
-        if (pos < 0) s = -__builtin_inff();
-        if (slot < a.n_slots) scores[row * a.ld + slot] = s;
-
-        if (block_max) {
-            float mx = s;
-            mx = fmaxf(mx, __shfl_xor(mx, 1));
-            mx = fmaxf(mx, __shfl_xor(mx, 2));
-            mx = fmaxf(mx, __shfl_xor(mx, 4));
-            if (mx == 0.0f) mx = 0.0f;
-            const int64_t blk = slot >> 3;
-            if ((t & 7) == 0 && blk < a.ld_bm) block_max[row * a.ld_bm + blk] = mx;
-        }
-        __syncthreads();
     }
-}
-
-template <int HI, int DI>
-__global__ __launch_bounds__(256) void transpose_q_kernel(const void* __restrict__ q, bool bf16,
-                                                          int64_t rows, float* __restrict__ qT) {
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gid >= rows * HI * DI) return;
-    const int64_t r = gid / (HI * DI);
-    const int rem = static_cast<int>(gid % (HI * DI));
-    const int h = rem / DI, c = rem % DI;
-    float v;
-    if (bf16)
-        v = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q)[gid]) << 16);
-    else
-        v = static_cast<const float*>(q)[gid];
-    qT[r * (HI * DI) + c * HI + h] = v;
 }
 
 template <int HI, int DI, bool KBF16>
 hipError_t launch_typed(const ScoreLaunch& p, hipStream_t st) {
     const int64_t rows = p.B * p.Tq;
-    {
-        const int64_t n = rows * HI * DI;
-        transpose_q_kernel<HI, DI><<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, st>>>(
-            p.q_idx, p.q_bf16, rows, p.qT);
-    }
     ScoreArgs a;
-    a.qT = p.qT; a.w = p.w; a.k = static_cast<const uint8_t*>(p.k_idx);
     a.cap = p.cap; a.Tq = p.Tq; a.ctx_len = p.ctx_len; a.q_pos = p.q_pos; a.m = p.m;
     a.pool = p.pool; a.P_b = p.P_b;
-    a.scores = p.scores; a.ld = p.ld; a.block_max = p.block_max; a.ld_bm = p.ld_bm;
+    a.ld = p.ld; a.ld_bm = p.ld_bm;
     a.n_slots = p.pool ? static_cast<int64_t>(p.P_b) * 8 : p.ld;
-    a.tiles_per_row = (a.n_slots + kTile - 1) / kTile;
-    const int64_t total = a.tiles_per_row * rows;
-    int64_t tpw = total / 2048;
-    if (tpw < 1) tpw = 1;
-    if (tpw > 64) tpw = 64;
-    a.tiles_per_wg = static_cast<int>(tpw);
-    const int64_t gx = (a.tiles_per_row + tpw - 1) / tpw;
+    a.units_per_row = (a.n_slots + kUnit - 1) / kUnit;
+    a.q_bf16 = p.q_bf16;
+    // enough workgroups to keep every CU at full occupancy (~2,048), at
+    // least 4 units (one per wave) each
+    int64_t upw = (a.units_per_row * rows + 2047) / 2048;
+    if (upw < kWaves) upw = kWaves;
+    a.units_per_wg = static_cast<int>(upw);
+    const int64_t gx = (a.units_per_row + upw - 1) / upw;
     if (gx == 0 || rows == 0) return hipGetLastError();
     score_kernel<HI, DI, KBF16><<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(rows)),
-                                  kTile, 0, st>>>(a.qT, a.w, a.k, a.scores, a.block_max, a);
+                                  kThreads, 0, st>>>(p.q_idx, p.w, static_cast<const uint8_t*>(p.k_idx),
+                                                      p.scores, p.block_max, a);
     return hipGetLastError();
 }
 

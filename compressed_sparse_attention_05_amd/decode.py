@@ -1,0 +1,166 @@
+"""Host-side composition of CSA2 decode layers over one shared KV set.
+
+Layer modes ("DeepSeek-V4.1-Flash KV Cache Compression" notes, section 2;
+"...reading a model through its three memory costs", section 03 table):
+  F  Full:    score every visible entry, take top-k, attend; the first Full
+              layer of the decoder also builds the candidate pool (block max
+              over 8 positions, top 2,048 blocks; notes section 3).
+  X  Reindex: score only the pool with the layer's own indexer query, take
+              top-k inside it, attend.
+  R  Reuse:   attend with the index list of the preceding F or X layer.
+Every layer attends with its own query and its own sliding-window KV; all
+layers read the same MXFP4 main-KV cache and indexer-K cache.
+
+DecodeStep pre-binds the ctypes argument structs of every library call of a
+step once, so a step costs one C call per kernel group and no Python-side
+allocation.  All arithmetic happens in libcsa2.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import binding as bd
+
+
+@dataclass
+class LayerInputs:
+    q: torch.Tensor                      # [B][H][D] bf16
+    swa: torch.Tensor                    # [B][W][D] bf16
+    q_idx: Optional[torch.Tensor] = None  # [B][1][H_I][d_I] (F and X layers)
+    w: Optional[torch.Tensor] = None      # [B][1][H_I] f32
+
+
+@dataclass
+class DecodeCache:
+    codes: torch.Tensor       # [B][cap][D/2] u8
+    scales: torch.Tensor      # [B][cap][D/16] u8
+    k_idx: torch.Tensor       # [B][cap][d_I]
+    ctx_len: torch.Tensor     # [B] int32 (entries visible after this step's write)
+    swa_len: torch.Tensor     # [B] int32
+
+
+class DecodeStep:
+    """One decode token for B sequences through a layer schedule.
+
+    schedule: string over {F, X, R}; the first F builds the pool when
+    build_pool is set (X layers need a pool: built here or passed in).
+    new_kv / new_kidx / dst_row: the token's main-KV row and indexer-K row,
+    written first (mxfp4_kv_write) so the new entry is visible to scoring.
+    """
+
+    def __init__(self, schedule: str, cache: DecodeCache, layers: List[LayerInputs], *, k: int,
+                 P_b: int = 2048, new_kv: Optional[torch.Tensor] = None,
+                 new_kidx: Optional[torch.Tensor] = None, dst_row: Optional[torch.Tensor] = None,
+                 pool: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                 build_pool: bool = True):
+        assert len(schedule) == len(layers)
+        self.schedule, self.cache, self.layers, self.k, self.P_b = schedule, cache, layers, k, P_b
+        B, cap, half = cache.codes.shape
+        D = half * 2
+        d_I = cache.k_idx.shape[-1]
+        dev = cache.codes.device
+        self.B, self.cap, self.D = B, cap, D
+        self.L = bd.lib()
+        self.calls = []          # (name, fn, args) in launch order
+        self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(D)
+        self._keep = []          # keep ctypes structs and tensors alive
+
+        # ---- write of the new token's entry
+        if new_kv is not None:
+            n_cache_rows = B * cap
+            kdt = bd._dtype(new_kidx, "new_kidx") if new_kidx is not None else 0
+            args = (bd._ptr(new_kv), bd._dtype(new_kv, "new_kv"), new_kv.shape[0], D, bd._ptr(dst_row),
+                    n_cache_rows, bd._ptr(cache.codes), bd._ptr(cache.scales), bd._ptr(new_kidx), kdt,
+                    d_I if new_kidx is not None else 0, bd._ptr(cache.k_idx), None)
+            self.calls.append(("write", self.L.mxfp4_kv_write, args))
+
+        self.scores = torch.empty((B, 1, cap), dtype=torch.float32, device=dev)
+        self.block_max = torch.empty((B, 1, (cap + 7) // 8), dtype=torch.float32, device=dev)
+        self.pool = pool if pool is not None else torch.full((B, 1, P_b), -1, dtype=torch.int32, device=dev)
+        self.pool_scores = torch.empty((B, 1, 8 * P_b), dtype=torch.float32, device=dev)
+        self.outs = [torch.empty((B, l.q.shape[1], D), dtype=torch.float32, device=dev) for l in layers]
+        self.idx_bufs = []
+        pool_built = pool is not None
+        cur_idx = None
+        for li, (mode, lay) in enumerate(zip(schedule, layers)):
+            if mode in "FX":
+                idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+                self.idx_bufs.append(idx)
+                use_pool = mode == "X"
+                if use_pool and not pool_built:
+                    raise ValueError("a Reindex layer needs a pool from an earlier Full layer")
+                want_bm = mode == "F" and build_pool and not pool_built
+                sa = bd.ScoreArgs(
+                    q_idx=lay.q_idx.data_ptr(), q_dtype=bd._dtype(lay.q_idx, "q_idx"), w=lay.w.data_ptr(),
+                    k_idx=cache.k_idx.data_ptr(), k_dtype=bd._dtype(cache.k_idx, "k_idx"), B=B, Tq=1,
+                    cap=cap, H_I=lay.q_idx.shape[2], d_I=d_I, ctx_len=cache.ctx_len.data_ptr(), q_pos=None,
+                    m=1, pool_blocks=self.pool.data_ptr() if use_pool else None,
+                    P_b=P_b if use_pool else 0,
+                    scores=(self.pool_scores if use_pool else self.scores).data_ptr(),
+                    ld_scores=8 * P_b if use_pool else cap,
+                    block_max=self.block_max.data_ptr() if want_bm else None)
+                nws = self.L.csa2_index_score_workspace_size(ctypes.byref(sa))
+                ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+                self._keep += [sa, ws]
+                self.calls.append((f"score{li}", self.L.csa2_index_score,
+                                   (ctypes.byref(sa), bd._ptr(ws), nws, None)))
+                if want_bm:
+                    nb = (cap + 7) // 8
+                    pws_n = self.L.csa2_build_candidate_pool_workspace_size(B, nb, P_b)
+                    pws = torch.empty(max(pws_n, 256), dtype=torch.uint8, device=dev)
+                    self._keep.append(pws)
+                    self.calls.append((f"pool{li}", self.L.csa2_build_candidate_pool,
+                                       (bd._ptr(self.block_max), B, nb, nb, P_b,
+                                        bd._ptr(self.pool), bd._ptr(pws), pws_n, None)))
+                    pool_built = True
+                if mode == "F" and pool_built and k <= P_b and 8 * P_b <= 32768:
+                    # the Full top-k lies inside the pool: select among its 8*P_b scores
+                    self.calls.append((f"topk{li}", self.L.csa2_topk_from_pool,
+                                       (bd._ptr(self.scores), B, cap, bd._ptr(self.pool), P_b, k,
+                                        bd._ptr(idx), None)))
+                else:
+                    src = self.pool_scores if use_pool else self.scores
+                    n = 8 * P_b if use_pool else cap
+                    tws_n = self.L.csa2_topk_workspace_size(B, n, k)
+                    tws = torch.empty(max(tws_n, 256), dtype=torch.uint8, device=dev)
+                    self._keep.append(tws)
+                    self.calls.append((f"topk{li}", self.L.csa2_topk,
+                                       (bd._ptr(src), B, n, n, k, bd._ptr(self.pool) if use_pool else None,
+                                        P_b if use_pool else 0, bd._ptr(idx), bd._ptr(tws), tws_n, None)))
+                cur_idx = idx
+            elif mode == "R":
+                if cur_idx is None:
+                    raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
+            else:
+                raise ValueError(f"unknown layer mode {mode!r}")
+            aa = bd.AttnArgs(q=lay.q.data_ptr(), q_dtype=bd._dtype(lay.q, "q"), codes=cache.codes.data_ptr(),
+                             scales=cache.scales.data_ptr(), cap=cap, idx=cur_idx.data_ptr(), k=k,
+                             swa=lay.swa.data_ptr(), swa_dtype=bd._dtype(lay.swa, "swa"), W=lay.swa.shape[1],
+                             swa_len=cache.swa_len.data_ptr(), B=B, H=lay.q.shape[1], D=D,
+                             sm_scale=self.sm_scale, out=self.outs[li].data_ptr())
+            nws = self.L.csa2_sparse_attn_decode_workspace_size(ctypes.byref(aa))
+            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+            self._keep += [aa, ws]
+            self.calls.append((f"attn{li}", self.L.csa2_sparse_attn_decode,
+                               (ctypes.byref(aa), bd._ptr(ws), nws, None)))
+            self.layer_idx = cur_idx
+
+    def run(self, stream=None, events=None):
+        """Enqueue the whole step on `stream` (default: torch's current).
+        events: optional dict name -> (start_event, end_event) to bracket calls."""
+        st = bd._stream(stream)
+        for name, fn, args in self.calls:
+            args = args[:-1] + (st,)
+            ev = events.get(name) if events else None
+            if ev is not None:
+                ev[0].record()
+            rc = fn(*args)
+            if ev is not None:
+                ev[1].record()
+            if rc != 0:
+                raise RuntimeError(f"{name}: libcsa2 error {rc}: {self.L.csa2_last_error().decode()}")

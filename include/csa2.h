@@ -74,7 +74,9 @@ const char *csa2_last_error(void);
  * codes      [n_cache_rows][D/2] uint8   (written at dst rows)
  * scales     [n_cache_rows][D/16] uint8  (written at dst rows)
  * idx_k_rows [n_rows][d_I] (idx_k_dtype) or NULL; when given, row i is
- *            copied unchanged to idx_k_cache[dst_row[i]] ([n_cache_rows][d_I]).
+ *            copied unchanged to flat row dst_row[i] of idx_k_cache, which
+ *            uses the TILED indexer-K layout described at csa2_index_score
+ *            (n_cache_rows % 64 == 0, d_I * elem_size % 16 == 0).
  * Requires D % 16 == 0, n_rows >= 0.
  * ------------------------------------------------------------------------ */
 int mxfp4_kv_write(const void *x, int x_dtype, int64_t n_rows, int32_t D,
@@ -101,6 +103,14 @@ int mxfp4_kv_write(const void *x, int x_dtype, int64_t n_rows, int32_t D,
  *     block_max[row][b] for b < ceil(ld_scores/8): the largest visible score
  *     in positions [8b, 8b+8) (-inf if none; zero reported as +0), the input
  *     of csa2_build_candidate_pool ([KVC] section 3, step 1).
+ * Indexer-K cache layout (TILED): k_idx holds B*cap flat rows (flat row
+ *     r = b*cap + pos, cap % 64 == 0) of d_I elements, grouped in tiles of
+ *     64 consecutive rows.  With NCH = d_I*elem_size/16 sixteen-byte chunks
+ *     per row, chunk c of flat row r is stored at byte offset
+ *         ((r / 64) * NCH + c) * 1024 + (r % 64) * 16.
+ *     A wave then reads chunk c of 64 positions as one contiguous 1 KiB
+ *     block and each lane receives its own row's chunk (the fma chain needs
+ *     one lane per position walking every channel in order).
  * Reindex mode (pool_blocks != NULL, [P_b] per row, ascending, -1 padded):
  *     scores[row][s] for s < 8*P_b scores position 8*pool[s/8] + s%8, or
  *     -inf when the block id is -1 or the position is not visible.
@@ -109,7 +119,7 @@ int mxfp4_kv_write(const void *x, int x_dtype, int64_t n_rows, int32_t D,
 typedef struct csa2_score_args {
     const void *q_idx;  int32_t q_dtype;  /* [B][Tq][H_I][d_I] */
     const float *w;                       /* [B][Tq][H_I] */
-    const void *k_idx;  int32_t k_dtype;  /* [B][cap][d_I] indexer-K cache */
+    const void *k_idx;  int32_t k_dtype;  /* B*cap rows of d_I, tiled layout */
     int64_t B, Tq, cap;
     int32_t H_I, d_I;
     const int32_t *ctx_len;               /* [B] */
@@ -146,11 +156,35 @@ int csa2_topk(const float *scores, int64_t rows, int64_t n, int64_t ld, int32_t 
  * with the largest block maxima, ties to the lower block id, as ascending
  * block ids padded with -1.  Pool positions are 8b..8b+7 of each block.
  * block_max [rows][ld], n_blocks <= ld; out_blocks [rows][P_b].
+ * For more than 32,768 blocks the selection runs through super-blocks of 8
+ * blocks: by the same argument as at csa2_topk_from_pool, the P_b best
+ * blocks all lie in the P_b best super-blocks (super-block value = max of its
+ * block maxima, ties to the lower id), so it first picks those and then the
+ * P_b best blocks among their 8*P_b blocks (exact, no workspace for
+ * P_b <= 2048 and n_blocks <= 262,144; other sizes use csa2_topk's path).
  * ------------------------------------------------------------------------ */
 size_t csa2_build_candidate_pool_workspace_size(int64_t rows, int64_t n_blocks, int32_t P_b);
 int csa2_build_candidate_pool(const float *block_max, int64_t rows, int64_t n_blocks, int64_t ld,
                               int32_t P_b, int32_t *out_blocks, void *ws, size_t ws_bytes,
                               void *stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_topk_from_pool - the Full-mode top-k of position-ordered score rows,
+ * found inside the row's candidate pool.  Requires k <= P_b (and
+ * 8*P_b <= 32768).  Then the k best positions (score desc, position asc)
+ * all lie in the pool: a position t in a block b outside the pool is
+ * preceded by the argmax position of each of the P_b pool blocks (each has
+ * a larger block max, or an equal one and a lower block id, hence a lower
+ * position), so t ranks below P_b >= k.  The result therefore equals
+ * csa2_topk over the whole row, bit for bit, while reading only the 8*P_b
+ * pool scores ([KVC] section 3: the first Full layer scores every position
+ * and builds the pool in the same pass).
+ * scores [rows][ld] (position order, -inf where invisible);
+ * pool_blocks [rows][P_b] ascending, -1 padded (csa2_build_candidate_pool);
+ * out_idx [rows][k] ascending positions, -1 padded.  No workspace.
+ * ------------------------------------------------------------------------ */
+int csa2_topk_from_pool(const float *scores, int64_t rows, int64_t ld, const int32_t *pool_blocks,
+                        int32_t P_b, int32_t k, int32_t *out_idx, void *stream);
 
 /* ------------------------------------------------------------------------
  * csa2_sparse_attn_decode - gather, dequantise, join with SWA, attend

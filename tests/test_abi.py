@@ -56,16 +56,26 @@ def test_topk_rejects_bad_arguments_on_host():
     assert L.csa2_topk(None, 0, 10, 10, 3, None, 0, None, None, 0, None) == 0  # nothing to do
 
 
-def test_score_unsupported_shape_and_workspace():
+def test_score_unsupported_shape_and_layout_checks():
     L = binding.lib()
     a = binding.ScoreArgs(q_idx=16, q_dtype=1, w=16, k_idx=16, k_dtype=1, B=1, Tq=1, cap=8, H_I=3,
                           d_I=128, ctx_len=16, m=1, scores=16, ld_scores=8)
     assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 2
     a.H_I = 8
-    assert L.csa2_index_score_workspace_size(ctypes.byref(a)) == 8 * 128 * 4
-    assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 3  # workspace missing
-    a.m = 0
+    assert L.csa2_index_score_workspace_size(ctypes.byref(a)) == 0
+    assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 1  # cap not a multiple of 64
+    assert "multiple of 64" in _err()
+    a.cap, a.m = 64, 0
     assert L.csa2_index_score(ctypes.byref(a), None, 0, None) == 1
+
+
+def test_topk_workspace_sizes():
+    L = binding.lib()
+    assert L.csa2_topk_workspace_size(8, 16384, 2048) == 0          # staged in LDS
+    big = L.csa2_topk_workspace_size(8, 131072, 2048)
+    assert big > 8 * 4096 * 4
+    assert L.csa2_topk(ctypes.c_void_p(256), 8, 131072, 131072, 2048, None, 0,
+                       ctypes.c_void_p(256), None, 0, None) == 3     # workspace missing
 
 
 def test_kv_write_and_attention_argument_checks():

@@ -83,7 +83,7 @@ def test_kv_write_bitexact(K, D, dtype):
 
 
 def test_kv_write_copies_indexer_rows(K):
-    n, D, d_I, cap = 10, 512, 128, 16
+    n, D, d_I, cap = 10, 512, 128, 128
     x = ci.gaussian(12, ci.TID_KV, (n, D), dtype=torch.bfloat16)
     kr = ci.gaussian(12, ci.TID_K_IDX, (n, d_I), dtype=torch.bfloat16)
     dst = torch.arange(n, dtype=torch.int64) + 3
@@ -92,8 +92,9 @@ def test_kv_write_copies_indexer_rows(K):
     kc = dev(torch.zeros((cap, d_I), dtype=torch.bfloat16))
     K.mxfp4_kv_write(dev(x), dev(dst), codes, scales, dev(kr), kc)
     torch.cuda.synchronize()
-    assert torch.equal(kc.cpu()[3:13], kr)
-    assert (kc.cpu()[:3].view(torch.int16) == 0).all()
+    rows = K.untile_indexer_cache(kc.view(1, cap, d_I))[0].cpu()
+    assert torch.equal(rows[3:13], kr)
+    assert (rows[:3].view(torch.int16) == 0).all() and (rows[13:].view(torch.int16) == 0).all()
 
 
 # ------------------------------------------------------------------ dequant through attention
@@ -135,7 +136,8 @@ def _score_case(K, seed, B, N, H_I, d_I, dtype, cap=None, ctx=None, ld=None):
     kc = ci.gaussian(seed, ci.TID_K_IDX, (B, cap, d_I), dtype=dtype)
     ctx = ctx if ctx is not None else [N] * B
     ctx_t = torch.tensor(ctx, dtype=torch.int32)
-    s, bm = K.csa2_index_score(dev(q), dev(w), dev(kc), dev(ctx_t), ld=ld, want_block_max=True)
+    s, bm = K.csa2_index_score(dev(q), dev(w), K.tile_indexer_cache(dev(kc)), dev(ctx_t), ld=ld,
+                               want_block_max=True)
     torch.cuda.synchronize()
     s, bm = s.cpu().numpy(), bm.cpu().numpy()
     for b in range(B):
@@ -153,23 +155,23 @@ def test_score_full_tiny_fp32(K):
 
 def test_score_full_bf16_ragged(K):
     # ragged visible lengths, a tail that is not a multiple of 8 or of the tile
-    _score_case(K, 102, B=3, N=5000, H_I=8, d_I=128, dtype=torch.bfloat16, cap=5003,
+    _score_case(K, 102, B=3, N=5000, H_I=8, d_I=128, dtype=torch.bfloat16, cap=5056,
                 ctx=[5003, 4099, 1], ld=5005)
 
 
 def test_score_4x64(K):
-    _score_case(K, 103, B=2, N=777, H_I=4, d_I=64, dtype=torch.bfloat16)
+    _score_case(K, 103, B=2, N=777, H_I=4, d_I=64, dtype=torch.bfloat16, cap=832, ctx=[777, 700])
 
 
 def test_score_exactly_summable_grid(K):
     # multiples of 2^-3 in [-4, 4]: every order gives the exact value; heavy ties
-    B, N, H_I, d_I = 2, 3000, 8, 128
+    B, N, H_I, d_I = 2, 3008, 8, 128
     g = torch.Generator().manual_seed(5)
     q = (torch.randint(-32, 33, (B, 1, H_I, d_I), generator=g) / 8.0).to(torch.bfloat16)
     kc = (torch.randint(-32, 33, (B, N, d_I), generator=g) / 8.0).to(torch.bfloat16)
     w = (torch.randint(0, 16, (B, 1, H_I), generator=g) / 16.0).float()
     ctx = torch.tensor([N, N - 13], dtype=torch.int32)
-    s, _ = K.csa2_index_score(dev(q), dev(w), dev(kc), dev(ctx))
+    s, _ = K.csa2_index_score(dev(q), dev(w), K.tile_indexer_cache(dev(kc)), dev(ctx))
     s = s.cpu().numpy()
     for b in range(B):
         exact = np.maximum(kc[b].double().numpy() @ q[b, 0].double().numpy().T, 0) @ w[b, 0].double().numpy()
@@ -200,6 +202,55 @@ def test_topk_random_and_ties(K):
         _topk_check(K, v, k)
 
 
+def test_topk_long_rows_fast_path_and_fallbacks(K):
+    rng = np.random.default_rng(9)
+    n = 100003
+    v = rng.standard_normal((6, n)).astype(np.float32)
+    v[1] = np.abs(v[1])                                   # scores >= 0 as in the method
+    v[2] = rng.integers(0, 5, n)                          # ~20K ties per value: tie list overflows
+    v[3] = 7.0                                            # everything equal
+    v[4, :] = -np.inf; v[4, 50000:50010] = 1.0            # 10 valid slots
+    v[5, ::3] = -np.inf
+    for k in (1, 2048, 4096, 5000):                       # 5000 > the in-LDS sort: fallback
+        _topk_check(K, v, k)
+    # the full-scan shape: 1M slots, k = 2048
+    big = np.abs(rng.standard_normal((2, 1 << 20))).astype(np.float32) * 10
+    big[1, :] = np.round(big[1, :])                       # ties across the threshold
+    _topk_check(K, big, 2048)
+
+
+def test_topk_from_pool_equals_full_topk(K):
+    rng = np.random.default_rng(10)
+    rows, n, P_b = 5, 70000, 2048
+    v = np.abs(rng.standard_normal((rows, n))).astype(np.float32) * 10
+    v[1] = np.round(v[1])                       # ties everywhere
+    v[2, 60001:] = -np.inf                      # invisible tail
+    v[3] = 1.0                                  # all equal
+    v[4, :] = -np.inf; v[4, 5:900:7] = 2.0      # fewer visible blocks than the pool
+    nb = (n + 7) // 8
+    bm = np.stack([oracle.block_max(v[r], int(np.sum(np.isfinite(v[r]))) if r in (2,) else n, nb)
+                   for r in range(rows)])
+    # block_max from the oracle for rows with an invisible tail uses vis; -inf entries
+    # elsewhere are simply never chosen
+    bm_t = dev(torch.from_numpy(bm))
+    pool = K.csa2_build_candidate_pool(bm_t, P_b)
+    for k in (1, 64, 2048):
+        got = K.csa2_topk_from_pool(dev(torch.from_numpy(v)), pool, k).cpu().numpy()
+        for r in range(rows):
+            assert np.array_equal(got[r], oracle.topk(v[r], k)), (r, k)
+
+
+def test_pool_through_superblocks(K):
+    rng = np.random.default_rng(11)
+    rows, nb, P_b = 3, 131075, 2048             # > 32768 blocks, ragged tail
+    bm = np.abs(rng.standard_normal((rows, nb))).astype(np.float32) * 20
+    bm[1] = np.round(bm[1] / 4)                 # heavy ties
+    bm[2, 100000:] = -np.inf
+    got = K.csa2_build_candidate_pool(dev(torch.from_numpy(bm)), P_b).cpu().numpy()
+    for r in range(rows):
+        assert np.array_equal(got[r], oracle.candidate_pool(bm[r], P_b)), r
+
+
 def test_topk_small_rows_exhaustive(K):
     rng = np.random.default_rng(8)
     rows = rng.integers(0, 3, (500, 9)).astype(np.float32)
@@ -209,7 +260,7 @@ def test_topk_small_rows_exhaustive(K):
 
 
 def test_pool_and_reindex_bitexact(K):
-    B, N, H_I, d_I, P_b, k = 2, 70000, 8, 128, 2048, 2048
+    B, N, H_I, d_I, P_b, k = 2, 70016, 8, 128, 2048, 2048
     q, w, kc, s, bm = _score_case(K, 104, B=B, N=N, H_I=H_I, d_I=d_I, dtype=torch.bfloat16,
                                   ctx=[N, N - 4001])
     pool = K.csa2_build_candidate_pool(dev(torch.from_numpy(bm)), P_b).cpu().numpy()
@@ -225,7 +276,7 @@ def test_pool_and_reindex_bitexact(K):
     w2 = ci.uniform(105, ci.TID_W, (B, 1, H_I))
     pool_t = dev(torch.from_numpy(np.stack(pools)[:, None]))
     ctx = torch.tensor([N, N - 4001], dtype=torch.int32)
-    ps, _ = K.csa2_index_score(dev(q2), dev(w2), dev(kc), dev(ctx), pool_blocks=pool_t)
+    ps, _ = K.csa2_index_score(dev(q2), dev(w2), K.tile_indexer_cache(dev(kc)), dev(ctx), pool_blocks=pool_t)
     idx = K.csa2_topk(ps, k, pool_blocks=pool_t).cpu().numpy()
     ps = ps.cpu().numpy()
     for b in range(B):
@@ -305,3 +356,27 @@ def test_attention_prefill_window(K):
         err = np.max(np.abs(out - want))
         print("prefill", q_pos0, s0, "err %.2e" % err, flush=True)
         assert err < ATOL
+
+
+def test_attention_prefill_long_split_sampled(K):
+    """Enough query units that each workgroup walks all 68 key tiles of a
+    query (index list restaged in windows); sampled queries vs the oracle."""
+    T, N, D, H, k, W = 520, 40000, 512, 64, 2048, 128
+    seed = 302
+    kv = ci.gaussian(seed, ci.TID_KV, (N, D), dtype=torch.float32)
+    codes, scales = oracle.mxfp4_encode(kv)
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.stack([torch.sort(torch.randperm(N, generator=g)[:k])[0] for _ in range(T)]).to(torch.int32)
+    idx[7, 100:300] = -1
+    q = ci.gaussian(seed, ci.TID_Q, (T, H, D), dtype=torch.bfloat16)
+    swa = ci.gaussian(seed, ci.TID_SWA, (T + W - 1, D), dtype=torch.bfloat16)
+    q_pos0 = 30000
+    out = K.csa2_sparse_attn_prefill(dev(q), dev(torch.from_numpy(codes)), dev(torch.from_numpy(scales)),
+                                     dev(idx), dev(swa), W, q_pos0).cpu().numpy()
+    errs = []
+    for t in (0, 7, 100, 333, 519):
+        want = oracle.attn_prefill(q[t:t + 1], codes, scales, idx[t:t + 1].numpy(), swa[t:t + W], W,
+                                   q_pos0 + t, 0, 1 / math.sqrt(D))
+        errs.append(np.max(np.abs(out[t] - want[0])))
+    print("sampled errs", ["%.2e" % e for e in errs], flush=True)
+    assert max(errs) < ATOL

@@ -522,3 +522,41 @@ def test_attention_large_logits_stay_finite():
     out = oracle.attn_decode(q, codes, scales, np.arange(n, dtype=np.int32), kv[:0], 0, scale)
     assert np.all(np.isfinite(out))
     assert np.max(np.abs(out - dec[j])) < 1e-6
+
+
+def test_full_topk_equals_topk_inside_pool_and_pool_through_superblocks():
+    """Two identities the GPU path relies on, checked by brute force on the
+    oracle: (1) with k <= P_b the Full top-k is the top-k among the pool's
+    positions; (2) the P_b best blocks are the P_b best among the blocks of
+    the P_b best 8-block super-blocks."""
+    rng = np.random.default_rng(17)
+    for trial in range(600):
+        n = int(rng.integers(8, 2500)); vis = int(rng.integers(1, n + 1))
+        P_b = int(rng.integers(1, 30)); k = int(rng.integers(1, P_b + 1))
+        if trial % 3 == 0:
+            s = rng.integers(0, 4, n).astype(np.float32)
+        elif trial % 3 == 1:
+            s = rng.standard_normal(n).astype(np.float32)
+        else:
+            s = np.round(rng.standard_normal(n) * 3).astype(np.float32)
+        s[vis:] = -np.inf
+        nb = (n + 7) // 8
+        bm = oracle.block_max(s, vis, nb)
+        pool = oracle.candidate_pool(bm, P_b)
+        slots = np.full(8 * P_b, -np.inf, np.float32)
+        for i, b in enumerate(pool):
+            for j in range(8):
+                if b >= 0 and 8 * b + j < n:
+                    slots[8 * i + j] = s[8 * b + j]
+        assert np.array_equal(oracle.pool_topk(slots, pool, k), oracle.topk(s, k)), trial
+        nsb = (nb + 7) // 8
+        sbm = np.array([bm[8 * i:8 * i + 8].max() for i in range(nsb)], np.float32)
+        sb = oracle.topk(sbm, P_b)
+        cand = np.full(8 * P_b, -np.inf, np.float32)
+        for i, x in enumerate(sb):
+            for j in range(8):
+                if x >= 0 and 8 * x + j < nb:
+                    cand[8 * i + j] = bm[8 * x + j]
+        sel = oracle.topk(cand, P_b)
+        pool2 = np.array([8 * sb[t // 8] + t % 8 if t >= 0 else -1 for t in sel], np.int32)
+        assert np.array_equal(pool2, pool), trial
