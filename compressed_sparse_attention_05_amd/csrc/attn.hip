@@ -8,15 +8,16 @@
 //     out_h = softmax_j(sm_scale * q_h . row_j) . rows
 // The latent (D channels) is both key and value; all heads share the rows.
 //
-// Work split: one workgroup = (unit, key split, block of 64 heads), 4 waves.
-// Wave w owns head group hg = w & 1 (32 heads) and channel half dh = w >> 1.
-// Keys stream in tiles of 32:
-//  1. all 256 threads gather the tile's rows and dequantise them to fp16 into
-//     LDS twice: key-major Kt[key][d] (for S) and Vt[step][grp][d][8 keys]
-//     (for P.V, so every MFMA operand is one 16-byte LDS read);
-//  2. S^T[key][head] over this wave's channel half with
+// Work split: one workgroup = (unit, key split, block of 64 heads), 2*NQ
+// waves (8 at D = 512).  Wave w owns head group hg = w & 1 (32 heads) and
+// channel slice dq = w >> 1 (D/NQ channels).  Keys stream in tiles of 32:
+//  1. all threads gather the tile's rows (prefetched one tile ahead) and
+//     dequantise them to fp16 into LDS twice: key-major Kt[key][d] (for S)
+//     and Vt[step][grp][cell(d)][8 keys] (for P.V, so every MFMA operand is
+//     one 16-byte LDS read; cell() is a bank swizzle);
+//  2. S^T[key][head] over this wave's channel slice with
 //     v_mfma_f32_32x32x16_f16 (A = key rows, B = q in registers), then the
-//     two channel halves are added through LDS (same order in both waves);
+//     NQ slices are added through LDS (same order in every wave);
 //  3. online softmax in base 2: each lane holds one head's 16 keys and its
 //     partner lane (l ^ 32) the other 16, so the statistics need one
 //     cross-lane max per tile;
@@ -41,6 +42,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kKT = 32;          // keys per tile
 constexpr int kMaxTilesPerSplit = 16;
+constexpr int kCombineMaxSplits = 64;  // key splits one combine block can merge
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -114,7 +116,9 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
     constexpr int KBUF = KT_BYTES > SP_BYTES ? KT_BYTES : SP_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[KBUF];
     __shared__ __attribute__((aligned(16))) _Float16 Vt[kKT * D];
-    __shared__ __attribute__((aligned(16))) int kvalid[kKT];
+    // 0 for a key that holds a row, -inf for an empty slot: added to the
+    // logits, so empty slots get probability exactly 0 without a branch
+    __shared__ __attribute__((aligned(16))) float kmask[kKT];
     __shared__ int32_t idx_s[kKT * kMaxTilesPerSplit];
     _Float16* Kt = reinterpret_cast<_Float16*>(kbuf);
     float* Spart = reinterpret_cast<float*>(kbuf);
@@ -266,13 +270,19 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
         }
     };
 
+    // Vt cell of channel d: the low three bits are XORed with the next three,
+    // so the dequantising lanes (channels 8j + c for lanes j) spread over all
+    // banks instead of landing 128 bytes apart, while any 8 consecutive
+    // channels read by the P.V operand still fill 8 distinct cells.
+    auto vcell = [](int d) { return d ^ ((d >> 3) & 7); };
+
     // dequantise this thread's KPT keys (values in h) into Kt and Vt
     auto store_tile = [&](const uint32_t (&h)[KPT][4], const int (&kind)[KPT]) {
         if (j < CH) {
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
                 const int key = key_of_i(i);
-                if (j == 0) kvalid[key] = kind[i] != 0 ? 1 : 0;
+                if (j == 0) kmask[key] = kind[i] != 0 ? 0.0f : -__builtin_inff();
                 *reinterpret_cast<uint4*>(&Kt[key * KROW + 8 * j]) =
                     make_uint4(h[i][0], h[i][1], h[i][2], h[i][3]);
             }
@@ -285,13 +295,15 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
                     lo4[q] = __builtin_amdgcn_perm(h[2 * q + 1][p], h[2 * q][p], 0x05040100u);
                     hi4[q] = __builtin_amdgcn_perm(h[2 * q + 1][p], h[2 * q][p], 0x07060302u);
                 }
-                _Float16* base = &Vt[((sg * 2 + gg) * D + 8 * j + 2 * p) * 8 + 4 * half];
+                const int grp = (sg * 2 + gg) * D;
+                _Float16* lo_p = &Vt[(grp + vcell(8 * j + 2 * p)) * 8 + 4 * half];
+                _Float16* hi_p = &Vt[(grp + vcell(8 * j + 2 * p + 1)) * 8 + 4 * half];
                 if (KPT == 8) {
-                    *reinterpret_cast<uint4*>(base) = make_uint4(lo4[0], lo4[1], lo4[KPT / 2 - 2], lo4[KPT / 2 - 1]);
-                    *reinterpret_cast<uint4*>(base + 8) = make_uint4(hi4[0], hi4[1], hi4[KPT / 2 - 2], hi4[KPT / 2 - 1]);
+                    *reinterpret_cast<uint4*>(lo_p) = make_uint4(lo4[0], lo4[1], lo4[KPT / 2 - 2], lo4[KPT / 2 - 1]);
+                    *reinterpret_cast<uint4*>(hi_p) = make_uint4(hi4[0], hi4[1], hi4[KPT / 2 - 2], hi4[KPT / 2 - 1]);
                 } else {
-                    *reinterpret_cast<uint2*>(base) = make_uint2(lo4[0], lo4[KPT / 2 - 1]);
-                    *reinterpret_cast<uint2*>(base + 8) = make_uint2(hi4[0], hi4[KPT / 2 - 1]);
+                    *reinterpret_cast<uint2*>(lo_p) = make_uint2(lo4[0], lo4[KPT / 2 - 1]);
+                    *reinterpret_cast<uint2*>(hi_p) = make_uint2(hi4[0], hi4[KPT / 2 - 1]);
                 }
             }
         }
@@ -309,27 +321,37 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
             const half8 kf = *reinterpret_cast<const half8*>(&Kt[(lane & 31) * KROW + d0]);
             s_acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s_acc, 0, 0, 0);
         }
-        int kv_ok[16];
+        float kmk[16];
         {
-            const int4* kv4 = reinterpret_cast<const int4*>(kvalid);
+            const float4* km4 = reinterpret_cast<const float4*>(kmask);
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 // rows 8*r4 + 4*(lane/32) + 0..3
-                const int4 v = kv4[2 * r4 + (lane >> 5)];
-                kv_ok[4 * r4] = v.x; kv_ok[4 * r4 + 1] = v.y; kv_ok[4 * r4 + 2] = v.z; kv_ok[4 * r4 + 3] = v.w;
+                const float4 v = km4[2 * r4 + (lane >> 5)];
+                kmk[4 * r4] = v.x; kmk[4 * r4 + 1] = v.y; kmk[4 * r4 + 2] = v.z; kmk[4 * r4 + 3] = v.w;
             }
         }
         __syncthreads();   // everyone done reading Kt before Spart overwrites it
+        // partials as [wave][r/4][lane][4]: one 16-byte LDS access per 4 rows
+        float4* Sp4 = reinterpret_cast<float4*>(Spart);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Spart[(wv * 16 + r) * 64 + lane] = s_acc[r];
+        for (int r4 = 0; r4 < 4; ++r4)
+            Sp4[(wv * 4 + r4) * 64 + lane] = make_float4(s_acc[4 * r4], s_acc[4 * r4 + 1],
+                                                         s_acc[4 * r4 + 2], s_acc[4 * r4 + 3]);
         __syncthreads();
         float t2[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float sum = Spart[(hg * 16 + r) * 64 + lane];
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float4 sum = Sp4[(hg * 4 + r4) * 64 + lane];
 #pragma unroll
-            for (int qq = 1; qq < NQ; ++qq) sum += Spart[((hg + 2 * qq) * 16 + r) * 64 + lane];
-            t2[r] = kv_ok[r] ? sum * a.c2 : -__builtin_inff();
+            for (int qq = 1; qq < NQ; ++qq) {
+                const float4 v = Sp4[((hg + 2 * qq) * 4 + r4) * 64 + lane];
+                sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+            }
+            t2[4 * r4] = fmaf(sum.x, a.c2, kmk[4 * r4]);
+            t2[4 * r4 + 1] = fmaf(sum.y, a.c2, kmk[4 * r4 + 1]);
+            t2[4 * r4 + 2] = fmaf(sum.z, a.c2, kmk[4 * r4 + 2]);
+            t2[4 * r4 + 3] = fmaf(sum.w, a.c2, kmk[4 * r4 + 3]);
         }
 
         // ---------------- 3. online softmax (base 2) with a lazy reference:
@@ -344,7 +366,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
         const bool grow = tmax > m_run + 8.0f || (m_run == -__builtin_inff() && tmax != -__builtin_inff());
         if (__ballot(grow) != 0) {
             const float m_new = grow ? tmax : m_run;
-            const float alpha = (m_run == -__builtin_inff()) ? 0.0f : exp2f(m_run - m_new);
+            const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             if (m_new != m_run) {
                 l_run *= alpha;
 #pragma unroll
@@ -362,11 +384,12 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
         } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const _Float16 p0 = static_cast<_Float16>(exp2f(t2[2 * q] - m_run));
-                const _Float16 p1 = static_cast<_Float16>(exp2f(t2[2 * q + 1] - m_run));
-                psum += static_cast<float>(p0) + static_cast<float>(p1);
-                pk[q] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, p0)) |
-                        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, p1)) << 16);
+                // v_exp_f32 directly: arguments are <= 8, and results too
+                // small for fp16 become 0 either way
+                const half2v ph = {static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[2 * q] - m_run)),
+                                   static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[2 * q + 1] - m_run))};
+                psum = __builtin_amdgcn_fdot2(ph, half2v{1.0f16, 1.0f16}, psum, false);
+                pk[q] = __builtin_bit_cast(uint32_t, ph);
             }
         }
         l_run += psum;
@@ -379,7 +402,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int d = dq * DQ + 32 * mt + (lane & 31);
-                const half8 vf = *reinterpret_cast<const half8*>(&Vt[((ks * 2 + (lane >> 5)) * D + d) * 8]);
+                const half8 vf = *reinterpret_cast<const half8*>(&Vt[((ks * 2 + (lane >> 5)) * D + vcell(d)) * 8]);
                 o_acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o_acc[mt], 0, 0, 0);
             }
         }
@@ -411,9 +434,9 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
             for (int i = 0; i < KPT; ++i) {
                 const uint32_t s16 = f16_bits(e4m3_val(pm_sc[i] & 0x7fu));
                 dequant8(pm_cw[i], s16 | (s16 << 16), h[i]);
+                // an empty slot keeps the (finite) values of the clamped row:
+                // its logit is -inf, so it enters P.V with weight exactly 0
                 kind[i] = pm_ok[i] ? 1 : 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h[i][e] = pm_ok[i] ? h[i][e] : 0u;
             }
             store_tile(h, kind);
         }
@@ -511,29 +534,46 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
                                                        int H, int hblocks, float* __restrict__ out) {
     constexpr int DQ = D / NQ, MT = DQ / 32;
     __shared__ float tile[32][33];
+    __shared__ float wgt[kCombineMaxSplits][32];   // exp2(m_s - m*) per split and head
+    __shared__ float inv_den[32];
     const int64_t ub = blockIdx.x;                 // unit * hblocks + hb
     const int wv = blockIdx.y / MT, mt = blockIdx.y % MT;
     const int hg = wv & 1, dqq = wv >> 1;
     const int t = threadIdx.x, r = t >> 6, ln = t & 63;
-    const int head_local = 32 * hg + (ln & 31);
-    const int dd = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-    const int64_t nat = ((wv * MT + mt) * 16 + r) * 64 + ln;
-    float mstar = -__builtin_inff();
-#pragma unroll 8
-    for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, ws_m[(ub * splits + s) * 64 + head_local]);
-    float num = 0.0f, den = 0.0f;
-    if (mstar != -__builtin_inff()) {
-#pragma unroll 8
+    // per-head split weights, once per block: thread t < 32 owns head 32hg+t
+    if (t < 32) {
+        const int hl = 32 * hg + t;
+        float mstar = -__builtin_inff();
+        for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, ws_m[(ub * splits + s) * 64 + hl]);
+        float den = 0.0f;
         for (int s = 0; s < splits; ++s) {
             const int64_t p = ub * splits + s;
-            const float ms = ws_m[p * 64 + head_local];
-            if (ms == -__builtin_inff()) continue;
-            const float wgt = exp2f(ms - mstar);
-            num += wgt * ws_o[p * (64 * D) + nat];
-            den += wgt * ws_l[p * 64 + head_local];
+            const float ms = ws_m[p * 64 + hl];
+            const float w = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mstar);
+            wgt[s][t] = w;
+            den += w * ws_l[p * 64 + hl];
         }
+        inv_den[t] = den > 0.0f ? 1.0f / den : 0.0f;
     }
-    tile[ln & 31][dd] = den > 0.0f ? num / den : 0.0f;
+    __syncthreads();
+    const int hcol = ln & 31;
+    const int dd = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+    const int64_t nat = ((wv * MT + mt) * 16 + r) * 64 + ln;
+    const float* po = ws_o + ub * splits * static_cast<int64_t>(64 * D) + nat;
+    float num = 0.0f;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+        const float o0 = po[(s + 0) * static_cast<int64_t>(64 * D)];
+        const float o1 = po[(s + 1) * static_cast<int64_t>(64 * D)];
+        const float o2 = po[(s + 2) * static_cast<int64_t>(64 * D)];
+        const float o3 = po[(s + 3) * static_cast<int64_t>(64 * D)];
+        num += wgt[s][hcol] * o0;
+        num += wgt[s + 1][hcol] * o1;
+        num += wgt[s + 2][hcol] * o2;
+        num += wgt[s + 3][hcol] * o3;
+    }
+    for (; s < splits; ++s) num += wgt[s][hcol] * po[s * static_cast<int64_t>(64 * D)];
+    tile[hcol][dd] = num * inv_den[hcol];
     __syncthreads();
     const int hb = static_cast<int>(ub % hblocks);
     const int64_t u = ub / hblocks;
@@ -552,6 +592,7 @@ SplitPlan plan(int64_t units, int H, int k, int W) {
     int64_t want = (512 + base - 1) / base;          // aim for ~512 workgroups
     int64_t max_splits = (p.n_tiles + 3) / 4;        // keep >= 4 tiles per split
     if (want > max_splits) want = max_splits;
+    if (want > kCombineMaxSplits) want = kCombineMaxSplits;
     if (want < 1) want = 1;
     p.tiles_per_split = static_cast<int>((p.n_tiles + want - 1) / want);
     if (p.tiles_per_split < 1) p.tiles_per_split = 1;

@@ -12,11 +12,13 @@
 // selection; a slot is chosen when key > T, or key == T and fewer than
 // need_T tied slots precede it.  Two paths:
 //
-//  * rows of up to 32,768 slots (pool scores, block maxima at 128K, small
-//    contexts): one 1,024-thread workgroup stages the whole row of keys in
-//    LDS, runs three histogram passes there, and emits the chosen slots in
-//    slot order with wave-ballot prefix counts (so ties resolve to the lowest
-//    slots and the output is sorted without a sort);
+//  * rows of up to 32,768 slots (pool scores, block maxima up to 256K
+//    positions, Reindex pools, small contexts): one 1,024-thread workgroup
+//    holds the row's keys in registers (a run of consecutive slots per
+//    thread), resolves the k-th key with 13-bit radix passes that start
+//    below the bits all keys share, and emits the chosen slots in slot order
+//    with workgroup prefix counts (so ties resolve to the lowest slots and
+//    the output is sorted without a sort);
 //  * longer rows (the Full scan at 128K-1M): many workgroups per row build a
 //    global 12-bit histogram, then every workgroup finds the threshold digit
 //    and appends the (key, slot) pairs at or above it to a per-row candidate
@@ -217,19 +219,31 @@ __device__ uint32_t count_valid(Get get, int64_t n, uint32_t* wave_tot) {
     return tot;
 }
 
-// ------------------------------------------------- LDS selection core
-// One 1,024-thread workgroup selects among up to kSelMax keys staged in
-// LDS.  Radix passes use 8-bit digits and one private 256-bin histogram per
-// wave (no cross-wave atomics; lanes of one wave meet only in crowded bins),
-// merged per pass.  Emission: thread t owns the run of R consecutive slots
-// [tR, tR + R); two workgroup scans give each thread its tie rank and output
-// offset, and it writes its chosen slots in order.
+// ------------------------------------------------- one-workgroup selection
+// Rows of up to kSelMax slots are selected by one 1,024-thread workgroup
+// with the keys in registers: thread t holds the run of R consecutive slots
+// [tR, tR + R) (R = 16 or 32).
+//  1. The nonempty count, smallest and largest key give the bits all keys
+//     share; radix passes start at the highest bit where they differ, so the
+//     first 13-bit digit already spreads the keys over the bins (scores share
+//     sign and most exponent bits, which a fixed top digit would spend a pass
+//     on).  Two passes usually resolve the k-th key.
+//  2. Each pass counts the keys that still match the resolved prefix into an
+//     LDS histogram; a workgroup scan over the bins from the top finds the
+//     digit holding the k-th key.
+//  3. Emission: two workgroup scans give each thread its tie rank and output
+//     offset, and it writes its chosen slots in order, so ties go to the
+//     lowest slots and the output is sorted without a sort.
 constexpr int kSelMax = 32768;
+constexpr int kSelBits = 13;
+constexpr int kSelBins = 1 << kSelBits;          // 8 bins per thread
+static_assert(kSelBins == 8 * kThreads, "bin ownership assumes 8 bins per thread");
 
 struct alignas(16) SelLds {
-    uint32_t keys[kSelMax];
-    uint32_t hist[kWaves][256];
+    uint32_t hist[kSelBins];
     uint32_t wave_tot[kWaves];
+    uint32_t wave_min[kWaves];
+    uint32_t wave_max[kWaves];
     uint32_t res[4];
 };
 
@@ -257,161 +271,163 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_t
     return before + incl - v;
 }
 
-// Choose the k best of keys[0, n) (0 = empty) and call out(rank, slot) for
-// each chosen slot in ascending slot order (rank = output position).
-// Returns the number chosen (min(k, #nonempty)).  keys[n, 1024*R) must be
-// zero, where R = run length (a multiple of 4).
-template <class Out>
-__device__ uint32_t select_core(SelLds& sh, int n, uint32_t k, Out out) {
+// Choose the k best keys of the workgroup's slots (thread t: slots
+// [tR, tR + R) in kk, 0 = empty) and call out(rank, j) for each chosen slot
+// tR + j in ascending slot order.  Returns min(k, #nonempty).
+template <int R, class Out>
+__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    uint32_t prefix = 0, need = 0, n_valid = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
+
+    // ---- 1. count, smallest and largest nonempty key
+    uint32_t cnt = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sh.hist[wv][lane * 4 + j] = 0u;
-        __syncthreads();
-        // Scores crowd into one or two digits (the top byte is sign and
-        // exponent), so each wave first adds its two most common digits with
-        // one ballot-counted atomic each; the remaining lanes add singly.
-        for (int base = 0; base < n; base += kThreads) {
-            const int i = base + tid;
-            const uint32_t key = i < n ? sh.keys[i] : 0u;
-            const bool ok = key != 0u && (pass == 0 || (key >> (shift + 8)) == prefix);
-            const uint32_t bin = (key >> shift) & 255u;
-            uint64_t act = __ballot(ok);
-#pragma unroll
-            for (int round = 0; round < 2; ++round) {
-                if (act != 0) {
-                    const int leader = __builtin_ctzll(act);
-                    const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
-                    const uint64_t same = __ballot(ok && bin == lb) & act;
-                    if (lane == leader) atomicAdd(&sh.hist[wv][lb], static_cast<uint32_t>(__popcll(same)));
-                    act &= ~same;
-                }
-            }
-            if ((act >> lane) & 1ull) atomicAdd(&sh.hist[wv][bin], 1u);
-        }
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t t = 0;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) t += sh.hist[w][tid];
-            sh.hist[0][tid] = t;
-        }
-        __syncthreads();
-        if (tid < 64) {
-            // lane l owns bins 255-4l .. 252-4l (descending)
-            uint32_t c[4], sum = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { c[j] = sh.hist[0][255 - 4 * lane - j]; sum += c[j]; }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
-            uint32_t nd = need;
-            if (pass == 0) {
-                const uint32_t total = __shfl(incl, 63);
-                nd = total < k ? total : k;
-                if (lane == 0) sh.res[2] = total;
-            }
-            const uint32_t excl = incl - sum;
-            if (nd > 0 && excl < nd && incl >= nd) {
-                uint32_t acc = excl;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (acc + c[j] >= nd) { sh.res[0] = 255u - 4u * lane - j; sh.res[1] = acc; break; }
-                    acc += c[j];
-                }
-            }
-            if (lane == 0) sh.res[3] = nd;
-        }
-        __syncthreads();
-        if (pass == 0) {
-            n_valid = sh.res[2];
-            need = sh.res[3];
-            if (need == 0) break;
-        }
-        prefix = (prefix << 8) | sh.res[0];
-        need -= sh.res[1];
-        __syncthreads();
+    for (int j = 0; j < R; ++j) {
+        cnt += kk[j] != 0u;
+        mn = (kk[j] != 0u && kk[j] < mn) ? kk[j] : mn;
+        mx = kk[j] > mx ? kk[j] : mx;
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        cnt += __shfl_xor(cnt, off);
+        const uint32_t omn = __shfl_xor(mn, off), omx = __shfl_xor(mx, off);
+        mn = omn < mn ? omn : mn;
+        mx = omx > mx ? omx : mx;
+    }
+    if (lane == 0) { sh.wave_tot[wv] = cnt; sh.wave_min[wv] = mn; sh.wave_max[wv] = mx; }
+    __syncthreads();
+    uint32_t n_valid = 0;
+    mn = 0xffffffffu; mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        n_valid += sh.wave_tot[w];
+        mn = sh.wave_min[w] < mn ? sh.wave_min[w] : mn;
+        mx = sh.wave_max[w] > mx ? sh.wave_max[w] : mx;
+    }
+    __syncthreads();
     const uint32_t k_eff = n_valid < k ? n_valid : k;
     if (k_eff == 0) return 0;
-    const uint32_t T = prefix;
-    const int R = ((n + kThreads * 4 - 1) / (kThreads * 4)) * 4;
-    const int r0 = tid * R;
-    uint32_t above = 0, ties = 0;
-    for (int i = r0; i < r0 + R; i += 4) {
-        const uint4 q = *reinterpret_cast<const uint4*>(&sh.keys[i]);
-        const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+
+    // ---- 2. radix passes below the shared prefix
+    uint32_t need = k_eff, T;
+    if (mn == mx) {
+        T = mn;                                    // every nonempty key is T
+    } else {
+        int top = 31 - __builtin_clz(mn ^ mx);     // highest bit not shared
+        uint64_t known = static_cast<uint64_t>(mn) >> (top + 1);
+        while (top >= 0) {
+            const int nb = top + 1 < kSelBits ? top + 1 : kSelBits;
+            const int shift = top + 1 - nb;
+            const uint32_t dmask = (1u << nb) - 1u;
+            // keys match the resolved prefix when their bits above `top`
+            // equal it (all keys do before the first pass below bit 31)
+            const bool match_all = top == 31;
+            const int pshift = match_all ? 0 : top + 1;
+            const uint32_t known32 = static_cast<uint32_t>(known);
+            for (int i = tid; i < kSelBins; i += kThreads) sh.hist[i] = 0u;
+            __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { above += kk[j] > T; ties += kk[j] == T; }
+            for (int j = 0; j < R; ++j) {
+                const bool ok = kk[j] != 0u && (match_all || (kk[j] >> pshift) == known32);
+                if (ok) atomicAdd(&sh.hist[(kk[j] >> shift) & dmask], 1u);
+                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            // thread t holds bins kSelBins-1-8t down to kSelBins-8-8t, so
+            // thread order is descending bin order
+            const int hb = kSelBins - 8 - 8 * tid;
+            const uint4 lo = *reinterpret_cast<const uint4*>(&sh.hist[hb]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(&sh.hist[hb + 4]);
+            const uint32_t c[8] = {hi.w, hi.z, hi.y, hi.x, lo.w, lo.z, lo.y, lo.x};
+            uint32_t sum = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum += c[i];
+            uint32_t tot;
+            const uint32_t excl = block_excl_scan(sum, sh.wave_tot, tot);
+            if (excl < need && excl + sum >= need) {
+                uint32_t acc = excl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (acc + c[i] >= need) { sh.res[0] = hb + 7 - i; sh.res[1] = acc; break; }
+                    acc += c[i];
+                }
+            }
+            __syncthreads();
+            known = (known << nb) | sh.res[0];
+            need -= sh.res[1];
+            top = shift - 1;
+            __syncthreads();
+        }
+        T = static_cast<uint32_t>(known);
     }
+
+    // ---- 3. ordered emission
+    uint32_t above = 0, ties = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) { above += kk[j] > T; ties += kk[j] == T; }
     uint32_t tmp;
     const uint32_t ties_before = block_excl_scan(ties, sh.wave_tot, tmp);
     uint32_t take = need > ties_before ? need - ties_before : 0u;
     if (take > ties) take = ties;
     uint32_t at = block_excl_scan(above + take, sh.wave_tot, tmp);
-    for (int i = r0; i < r0 + R; i += 4) {
-        const uint4 q = *reinterpret_cast<const uint4*>(&sh.keys[i]);
-        const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool tie_pick = kk[j] == T && take > 0;
-            if (kk[j] > T || tie_pick) {
-                if (tie_pick) --take;
-                if (at < k) out(at, i + j);
-                ++at;
-            }
+    for (int j = 0; j < R; ++j) {
+        const bool tie_pick = kk[j] == T && take > 0;
+        if (kk[j] > T || tie_pick) {
+            if (tie_pick) --take;
+            if (at < k) out(at, j);
+            ++at;
         }
+        if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     return k_eff;
 }
 
-// Zero keys[n, round_up(n, 4096)) so every run is fully defined.
-__device__ __forceinline__ void pad_keys(SelLds& sh, int n) {
-    const int padded = ((n + kThreads * 4 - 1) / (kThreads * 4)) * kThreads * 4;
-    for (int i = n + threadIdx.x; i < padded; i += kThreads) sh.keys[i] = 0u;
+// Keys of slots [i0, i0 + R) of a float row with n valid entries: 16-byte
+// loads when the run is aligned and complete, else element loads.
+template <int R>
+__device__ __forceinline__ void load_run_keys(const float* __restrict__ row, int64_t i0, int64_t n,
+                                              uint32_t (&kk)[R]) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(row + i0) & 15u) == 0) && i0 + R <= n;
+    if (vec) {
+#pragma unroll
+        for (int j = 0; j < R; j += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + i0 + j);
+            kk[j] = key_of(v.x); kk[j + 1] = key_of(v.y); kk[j + 2] = key_of(v.z); kk[j + 3] = key_of(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < R; ++j) kk[j] = (i0 + j < n) ? key_of(row[i0 + j]) : 0u;
+    }
 }
 
 // ---------------------------------------------------------------- small rows
 // Rows of up to kSelMax slots: slot order, or pool slots (-> positions).
+template <int R>
 __global__ __launch_bounds__(kThreads) void topk_small_kernel(const float* __restrict__ scores, int64_t n,
                                                               int64_t ld, int k,
                                                               const int32_t* __restrict__ pool, int P_b,
                                                               int32_t* __restrict__ out) {
     __shared__ SelLds sh;
     const int64_t row = blockIdx.x;
-    const float* s = scores + row * ld;
     int32_t* o = out + row * static_cast<int64_t>(k);
     const int32_t* prow = pool ? pool + row * static_cast<int64_t>(P_b) : nullptr;
-    const int nn = static_cast<int>(n);
-    for (int base = 0; base < nn; base += 8 * kThreads) {
-        float v[8];
+    uint32_t kk[R];
+    const int r0 = threadIdx.x * R;
+    load_run_keys<R>(scores + row * ld, r0, n, kk);
+    int32_t blk[R / 8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = base + j * kThreads + threadIdx.x;
-            v[j] = i < nn ? s[i] : -__builtin_inff();
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = base + j * kThreads + threadIdx.x;
-            if (i < nn) sh.keys[i] = key_of(v[j]);
-        }
-    }
-    pad_keys(sh, nn);
-    __syncthreads();
-    const uint32_t got = select_core(sh, nn, static_cast<uint32_t>(k), [&](uint32_t r, int slot) {
-        o[r] = prow ? prow[slot >> 3] * 8 + (slot & 7) : slot;
+    for (int q = 0; q < R / 8; ++q) blk[q] = (prow && r0 / 8 + q < P_b) ? prow[r0 / 8 + q] : 0;
+    const uint32_t got = select_run<R>(kk, static_cast<uint32_t>(k), sh, [&](uint32_t r, int j) {
+        o[r] = prow ? blk[j >> 3] * 8 + (j & 7) : r0 + j;
     });
     for (int i = static_cast<int>(got) + threadIdx.x; i < k; i += kThreads) o[i] = -1;
 }
 
 // Full-mode top-k through the candidate pool: scores are in position order;
-// slot s of the pool is position 8*pool[s/8] + s%8.
+// slot s of the pool is position 8*pool[s/8] + s%8.  Thread t gathers the
+// R/8 pool blocks of its run (two 16-byte loads per block when aligned).
+template <int R>
 __global__ __launch_bounds__(kThreads) void topk_from_pool_kernel(const float* __restrict__ scores, int64_t ld,
                                                                   const int32_t* __restrict__ pool, int P_b,
                                                                   int k, int32_t* __restrict__ out) {
@@ -420,29 +436,31 @@ __global__ __launch_bounds__(kThreads) void topk_from_pool_kernel(const float* _
     const float* s = scores + row * ld;
     const int32_t* prow = pool + row * static_cast<int64_t>(P_b);
     int32_t* o = out + row * static_cast<int64_t>(k);
-    const int n = 8 * P_b;
-    for (int base = 0; base < n; base += 8 * kThreads) {
-        float v[8];
+    const bool aligned = (reinterpret_cast<uintptr_t>(s) & 31u) == 0;
+    constexpr int NB = R / 8;
+    const int b0 = threadIdx.x * NB;
+    int32_t blk[NB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = base + j * kThreads + threadIdx.x;
-            v[j] = -__builtin_inff();
-            if (i < n) {
-                const int32_t b = prow[i >> 3];
-                const int64_t pos = static_cast<int64_t>(b) * 8 + (i & 7);
-                if (b >= 0 && pos < ld) v[j] = s[pos];
-            }
-        }
+    for (int q = 0; q < NB; ++q) blk[q] = (b0 + q < P_b) ? prow[b0 + q] : -1;
+    uint32_t kk[R];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = base + j * kThreads + threadIdx.x;
-            if (i < n) sh.keys[i] = key_of(v[j]);
+    for (int q = 0; q < NB; ++q) {
+        const int64_t p0 = static_cast<int64_t>(blk[q]) * 8;
+        if (blk[q] >= 0 && aligned && p0 + 8 <= ld) {
+            const float4 v0 = *reinterpret_cast<const float4*>(s + p0);
+            const float4 v1 = *reinterpret_cast<const float4*>(s + p0 + 4);
+            kk[8 * q + 0] = key_of(v0.x); kk[8 * q + 1] = key_of(v0.y);
+            kk[8 * q + 2] = key_of(v0.z); kk[8 * q + 3] = key_of(v0.w);
+            kk[8 * q + 4] = key_of(v1.x); kk[8 * q + 5] = key_of(v1.y);
+            kk[8 * q + 6] = key_of(v1.z); kk[8 * q + 7] = key_of(v1.w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                kk[8 * q + e] = (blk[q] >= 0 && p0 + e < ld) ? key_of(s[p0 + e]) : 0u;
         }
     }
-    pad_keys(sh, n);
-    __syncthreads();
-    const uint32_t got = select_core(sh, n, static_cast<uint32_t>(k), [&](uint32_t r, int slot) {
-        o[r] = prow[slot >> 3] * 8 + (slot & 7);
+    const uint32_t got = select_run<R>(kk, static_cast<uint32_t>(k), sh, [&](uint32_t r, int j) {
+        o[r] = blk[j >> 3] * 8 + (j & 7);
     });
     for (int i = static_cast<int>(got) + threadIdx.x; i < k; i += kThreads) o[i] = -1;
 }
@@ -450,75 +468,71 @@ __global__ __launch_bounds__(kThreads) void topk_from_pool_kernel(const float* _
 // Candidate pool: the P_b best blocks by block max.  Up to kSelMax blocks
 // directly; beyond that through super-blocks of 8 blocks (the P_b best
 // blocks all lie in the P_b best super-blocks by super-block max, ties to
-// the lower id), so both stages stay in LDS.
+// the lower id), so both stages stay in one workgroup.
 constexpr int kPoolMax = 2048;
 
+template <int R>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const float* __restrict__ bmax, int64_t n_blocks,
                                                         int64_t ld, int P_b, int32_t* __restrict__ out) {
+    __shared__ SelLds sh;
+    const int64_t row = blockIdx.x;
+    const float* bm = bmax + row * ld;
+    int32_t* o = out + row * static_cast<int64_t>(P_b);
+    const int64_t r0 = static_cast<int64_t>(threadIdx.x) * R;
+    uint32_t kk[R];
+    load_run_keys<R>(bm, r0, n_blocks, kk);
+    const uint32_t got = select_run<R>(kk, static_cast<uint32_t>(P_b), sh,
+                                       [&](uint32_t r, int j) { o[r] = static_cast<int32_t>(r0) + j; });
+    for (int i = static_cast<int>(got) + threadIdx.x; i < P_b; i += kThreads) o[i] = -1;
+}
+
+// More than kSelMax blocks: stage 1 selects the P_b best super-blocks (8
+// blocks each) by super-block max, stage 2 the P_b best blocks among their
+// 8*P_b blocks.
+template <int R>
+__global__ __launch_bounds__(kThreads) void pool_super_kernel(const float* __restrict__ bmax, int64_t n_blocks,
+                                                              int64_t ld, int P_b, int32_t* __restrict__ out) {
     __shared__ SelLds sh;
     __shared__ int32_t sup[kPoolMax];
     const int64_t row = blockIdx.x;
     const float* bm = bmax + row * ld;
     int32_t* o = out + row * static_cast<int64_t>(P_b);
-    uint32_t got;
-    if (n_blocks <= kSelMax) {
-        const int n = static_cast<int>(n_blocks);
-        for (int base = 0; base < n; base += 8 * kThreads) {
-            float v[8];
+    const int64_t r0 = static_cast<int64_t>(threadIdx.x) * R;
+    {
+        // stage 1: thread t owns super-blocks [tR, tR + R); four in flight
+        uint32_t kk[R];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = base + j * kThreads + threadIdx.x;
-                v[j] = i < n ? bm[i] : -__builtin_inff();
-            }
+        for (int j = 0; j < R; ++j) {
+            uint32_t e8[8];
+            load_run_keys<8>(bm, (r0 + j) * 8, n_blocks, e8);
+            uint32_t m = 0u;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = base + j * kThreads + threadIdx.x;
-                if (i < n) sh.keys[i] = key_of(v[j]);
-            }
+            for (int e = 0; e < 8; ++e) m = e8[e] > m ? e8[e] : m;
+            kk[j] = m;
+            if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
-        pad_keys(sh, n);
-        __syncthreads();
-        got = select_core(sh, n, static_cast<uint32_t>(P_b), [&](uint32_t r, int slot) { o[r] = slot; });
-    } else {
-        // stage 1: super-block keys = max of 8 block keys
-        const int nsb = static_cast<int>((n_blocks + 7) / 8);
-        for (int base = 0; base < nsb; base += 4 * kThreads) {
-            float v[4][8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sb = base + j * kThreads + threadIdx.x;
-                const int64_t b0 = static_cast<int64_t>(sb) * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    v[j][e] = (sb < nsb && b0 + e < n_blocks) ? bm[b0 + e] : -__builtin_inff();
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sb = base + j * kThreads + threadIdx.x;
-                if (sb >= nsb) continue;
-                uint32_t m = 0u;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { const uint32_t kk = key_of(v[j][e]); m = kk > m ? kk : m; }
-                sh.keys[sb] = m;
-            }
-        }
-        pad_keys(sh, nsb);
         for (int i = threadIdx.x; i < P_b; i += kThreads) sup[i] = -1;
         __syncthreads();
-        select_core(sh, nsb, static_cast<uint32_t>(P_b), [&](uint32_t r, int slot) { sup[r] = slot; });
-        // stage 2: the 8*P_b blocks of the chosen super-blocks (ascending ids)
-        const int n2 = 8 * P_b;
-        for (int i = threadIdx.x; i < n2; i += kThreads) {
-            const int32_t sb = sup[i >> 3];
-            const int64_t b = static_cast<int64_t>(sb) * 8 + (i & 7);
-            sh.keys[i] = (sb >= 0 && b < n_blocks) ? key_of(bm[b]) : 0u;
-        }
-        pad_keys(sh, n2);
+        select_run<R>(kk, static_cast<uint32_t>(P_b), sh,
+                      [&](uint32_t r, int j) { sup[r] = static_cast<int32_t>(r0) + j; });
         __syncthreads();
-        got = select_core(sh, n2, static_cast<uint32_t>(P_b), [&](uint32_t r, int slot) {
-            o[r] = sup[slot >> 3] * 8 + (slot & 7);
-        });
     }
+    // stage 2: the 8*P_b blocks of the chosen super-blocks (ascending ids);
+    // thread t takes slots [16t, 16t + 16) = super-blocks 2t and 2t+1
+    uint32_t k2[16];
+    int32_t sb2[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int si = 2 * threadIdx.x + q;
+        sb2[q] = si < P_b ? sup[si] : -1;
+        uint32_t e8[8];
+        load_run_keys<8>(bm, static_cast<int64_t>(sb2[q] >= 0 ? sb2[q] : 0) * 8, n_blocks, e8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k2[8 * q + e] = sb2[q] >= 0 ? e8[e] : 0u;
+    }
+    const uint32_t got = select_run<16>(k2, static_cast<uint32_t>(P_b), sh, [&](uint32_t r, int j) {
+        o[r] = sb2[j >> 3] * 8 + (j & 7);
+    });
     for (int i = static_cast<int>(got) + threadIdx.x; i < P_b; i += kThreads) o[i] = -1;
 }
 
@@ -702,7 +716,10 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float* __res
 hipError_t launch_topk_from_pool(const float* scores, int64_t rows, int64_t ld, const int32_t* pool, int P_b,
                                  int k, int32_t* out, hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    topk_from_pool_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(scores, ld, pool, P_b, k, out);
+    if (8 * P_b <= 16 * kThreads)
+        topk_from_pool_kernel<16><<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(scores, ld, pool, P_b, k, out);
+    else
+        topk_from_pool_kernel<32><<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(scores, ld, pool, P_b, k, out);
     return hipGetLastError();
 }
 
@@ -713,7 +730,15 @@ bool pool_in_lds(int64_t n_blocks, int P_b) {
 hipError_t launch_pool(const float* bmax, int64_t rows, int64_t n_blocks, int64_t ld, int P_b, int32_t* out,
                        hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    pool_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(bmax, n_blocks, ld, P_b, out);
+    const dim3 grid(static_cast<unsigned>(rows));
+    if (n_blocks <= 16 * kThreads)
+        pool_kernel<16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld, P_b, out);
+    else if (n_blocks <= kSelMax)
+        pool_kernel<32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld, P_b, out);
+    else if ((n_blocks + 7) / 8 <= 16 * kThreads)
+        pool_super_kernel<16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld, P_b, out);
+    else
+        pool_super_kernel<32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld, P_b, out);
     return hipGetLastError();
 }
 
@@ -727,7 +752,10 @@ hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int64_t ld,
                        const int32_t* pool, int P_b, int32_t* out, void* ws, hipStream_t st) {
     if (rows == 0) return hipSuccess;
     if (n <= kSmallMax) {
-        topk_small_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(scores, n, ld, k, pool, P_b, out);
+        if (n <= 16 * kThreads)
+            topk_small_kernel<16><<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(scores, n, ld, k, pool, P_b, out);
+        else
+            topk_small_kernel<32><<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(scores, n, ld, k, pool, P_b, out);
         return hipGetLastError();
     }
     LongWs w;
