@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the CSA2 decode hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--secondary]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
 
 A step is one decode token for B sequences through the whole path of the
 workload's layer schedule: mxfp4_kv_write of the token's entry, the Full
@@ -13,7 +13,9 @@ from the previous one.
 
 Prints ONE JSON line: queries/s for the workload, the dominant kernel's
 roofline (the Full-mode indexer scan, timed live with HIP events on the
-stream it runs on), and the CPU oracle timed on a bounded sample.
+stream it runs on), the CPU oracle timed on a bounded sample, and under
+"secondary" the two 1M-context decode workloads (decoder block 2 with its
+Reindex layer, and the full 20-layer step at B=64).
 """
 from __future__ import annotations
 
@@ -160,8 +162,10 @@ def traffic_for(workload_name):
 
 
 # --------------------------------------------------------------------------
-def run_workload(K, w: ci.Workload, steps: int, warmup: int, dev):
-    sets = [InputSet(K, w, w.seed + 100 * i, dev) for i in range(2)]
+def run_workload(K, w: ci.Workload, steps: int, warmup: int, dev, n_sets: int = 2):
+    """Time `steps` decode steps.  n_sets independent input sets alternate
+    (two when a step's working set could sit in the 256 MiB MALL)."""
+    sets = [InputSet(K, w, w.seed + 100 * i, dev) for i in range(n_sets)]
     pools = [build_pool_for(K, w, s) if "X" in w.schedule and "F" not in w.schedule else None
              for s in sets]
     runners = [make_step(K, w, s, pool=p) for s, p in zip(sets, pools)]
@@ -170,7 +174,7 @@ def run_workload(K, w: ci.Workload, steps: int, warmup: int, dev):
     if scan_name is None:
         scan_name = next(f"score{i}" for i, m in enumerate(w.schedule) if m == "X")
     for i in range(warmup):
-        runners[i % 2].run()
+        runners[i % n_sets].run()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
@@ -180,7 +184,7 @@ def run_workload(K, w: ci.Workload, steps: int, warmup: int, dev):
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        runners[i % 2].run(events={scan_name: evs[i]})
+        runners[i % n_sets].run(events={scan_name: evs[i]})
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -269,8 +273,8 @@ def main(argv=None):
     ap.add_argument("--cpu-queries", type=int, default=8, help="oracle sample size (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--secondary", action="store_true",
-                    help="also time the 1M-context decode workloads (extra setup time)")
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="skip the 1M-context decode workloads")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -342,16 +346,28 @@ def main(argv=None):
         }
     if args.secondary:
         sec = []
-        for name in (ci.DECODE_1M_BLOCK2.name,):
+        # (workload, input sets, timed steps): the 20-layer step moves ~19 GB,
+        # far beyond the MALL, so one input set suffices there
+        for name, n_sets, steps2 in ((ci.DECODE_1M_BLOCK2.name, 2, max(20, args.steps // 4)),
+                                     (ci.DECODE_1M_20L.name, 1, 10)):
             w2 = ci.WORKLOADS[name]
             del r
             torch.cuda.empty_cache()
             print(f"# setting up {w2.name}", file=sys.stderr, flush=True)
-            r = run_workload(K, w2, max(20, args.steps // 4), 5, dev)
+            t_setup = time.perf_counter()
+            r = run_workload(K, w2, steps2, 3, dev, n_sets=n_sets)
+            print(f"# {w2.name}: {time.perf_counter() - t_setup:.1f} s incl. setup", file=sys.stderr, flush=True)
             ms2 = r["ms_per_step"]
-            sec.append({"workload": w2.name, "value": round(w2.B / (ms2 * 1e-3), 1), "unit": "queries/s",
+            alg2 = algorithmic_bytes_per_query(w2) * w2.B
+            scan_b = (scan_bytes_per_launch(w2) if "F" in w2.schedule
+                      else w2.B * (w2.P_b * 8 * w2.d_I * 2 + w2.P_b * 4 + w2.H_I * w2.d_I * 2 + w2.H_I * 4))
+            sec.append({"workload": w2.name, "batch": w2.B, "context": w2.N, "schedule": w2.schedule,
+                        "value": round(w2.B / (ms2 * 1e-3), 1), "unit": "queries/s",
                         "ms_per_step": round(ms2, 4),
-                        "algorithmic_GBps": round(algorithmic_bytes_per_query(w2) * w2.B / (ms2 * 1e-3) / 1e9, 1)})
+                        "algorithmic_GBps": round(alg2 / (ms2 * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(alg2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "scan": {"kernel": r["scan_name"], "us": round(r["scan_ms"] * 1e3, 2),
+                                 "GBps": round(scan_b / (r["scan_ms"] * 1e-3) / 1e9, 1)}})
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
     return 0

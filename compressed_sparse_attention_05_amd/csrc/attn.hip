@@ -534,45 +534,60 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
                                                        int H, int hblocks, float* __restrict__ out) {
     constexpr int DQ = D / NQ, MT = DQ / 32;
     __shared__ float tile[32][33];
-    __shared__ float wgt[kCombineMaxSplits][32];   // exp2(m_s - m*) per split and head
+    __shared__ float wgt[kCombineMaxSplits][32];   // m_s, then exp2(m_s - m*), per split and head
+    __shared__ float lsum[kCombineMaxSplits][32];
     __shared__ float inv_den[32];
     const int64_t ub = blockIdx.x;                 // unit * hblocks + hb
     const int wv = blockIdx.y / MT, mt = blockIdx.y % MT;
     const int hg = wv & 1, dqq = wv >> 1;
     const int t = threadIdx.x, r = t >> 6, ln = t & 63;
-    // per-head split weights, once per block: thread t < 32 owns head 32hg+t
-    if (t < 32) {
-        const int hl = 32 * hg + t;
-        float mstar = -__builtin_inff();
-        for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, ws_m[(ub * splits + s) * 64 + hl]);
-        float den = 0.0f;
-        for (int s = 0; s < splits; ++s) {
-            const int64_t p = ub * splits + s;
-            const float ms = ws_m[p * 64 + hl];
-            const float w = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mstar);
-            wgt[s][t] = w;
-            den += w * ws_l[p * 64 + hl];
-        }
-        inv_den[t] = den > 0.0f ? 1.0f / den : 0.0f;
-    }
-    __syncthreads();
     const int hcol = ln & 31;
     const int dd = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
     const int64_t nat = ((wv * MT + mt) * 16 + r) * 64 + ln;
     const float* po = ws_o + ub * splits * static_cast<int64_t>(64 * D) + nat;
-    float num = 0.0f;
-    int s = 0;
-    for (; s + 4 <= splits; s += 4) {
-        const float o0 = po[(s + 0) * static_cast<int64_t>(64 * D)];
-        const float o1 = po[(s + 1) * static_cast<int64_t>(64 * D)];
-        const float o2 = po[(s + 2) * static_cast<int64_t>(64 * D)];
-        const float o3 = po[(s + 3) * static_cast<int64_t>(64 * D)];
-        num += wgt[s][hcol] * o0;
-        num += wgt[s + 1][hcol] * o1;
-        num += wgt[s + 2][hcol] * o2;
-        num += wgt[s + 3][hcol] * o3;
+    constexpr int64_t PS = 64 * D;                 // partial stride
+    // the first 16 splits' partials are loaded before the weights are
+    // formed, so the two latencies overlap
+    constexpr int kEarly = 16;
+    float oe[kEarly];
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i) oe[i] = i < splits ? po[i * PS] : 0.0f;
+    // per-head split weights, once per block: thread t loads (split t/32,
+    // head 32hg + t%32), then thread t < 32 reduces over the splits in LDS
+    {
+        const int h = t & 31;
+        for (int s = t >> 5; s < splits; s += 32) {
+            const int64_t p = (ub * splits + s) * 64 + 32 * hg + h;
+            wgt[s][h] = ws_m[p];
+            lsum[s][h] = ws_l[p];
+        }
     }
-    for (; s < splits; ++s) num += wgt[s][hcol] * po[s * static_cast<int64_t>(64 * D)];
+    __syncthreads();
+    if (t < 32) {
+        float mstar = -__builtin_inff();
+        for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, wgt[s][t]);
+        float den = 0.0f;
+        for (int s = 0; s < splits; ++s) {
+            const float ms = wgt[s][t];
+            const float w = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mstar);
+            wgt[s][t] = w;
+            den += w * lsum[s][t];
+        }
+        inv_den[t] = den > 0.0f ? 1.0f / den : 0.0f;
+    }
+    __syncthreads();
+    float num = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i) num += i < splits ? wgt[i][hcol] * oe[i] : 0.0f;
+    int s = kEarly;
+    for (; s + 8 <= splits; s += 8) {
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = po[(s + i) * PS];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) num += wgt[s + i][hcol] * o[i];
+    }
+    for (; s < splits; ++s) num += wgt[s][hcol] * po[s * PS];
     tile[hcol][dd] = num * inv_den[hcol];
     __syncthreads();
     const int hb = static_cast<int>(ub % hblocks);
