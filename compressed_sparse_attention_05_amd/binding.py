@@ -45,6 +45,12 @@ class AttnPrefillArgs(ctypes.Structure):
 
 
 # Every function the header declares, with its ctypes signature.
+class PrefillTopkArgs(ctypes.Structure):
+    _fields_ = [("q_idx", P), ("q_dtype", i32), ("w", P), ("k_idx", P), ("k_dtype", i32),
+                ("T", i64), ("cap", i64), ("H_I", i32), ("d_I", i32), ("ctx_len", i32),
+                ("q_pos0", i64), ("m", i32), ("k", i32), ("out_idx", P)]
+
+
 SIGNATURES = {
     "csa2_version": (ctypes.c_char_p, []),
     "csa2_last_error": (ctypes.c_char_p, []),
@@ -60,6 +66,8 @@ SIGNATURES = {
     "csa2_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), P, ctypes.c_size_t, P]),
     "csa2_sparse_attn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnPrefillArgs)]),
     "csa2_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(AttnPrefillArgs), P, ctypes.c_size_t, P]),
+    "csa2_prefill_topk_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(PrefillTopkArgs)]),
+    "csa2_prefill_topk": (ctypes.c_int, [ctypes.POINTER(PrefillTopkArgs), P, ctypes.c_size_t, P]),
 }
 
 _lib = None
@@ -305,4 +313,27 @@ def csa2_sparse_attn_prefill(q, codes, scales, idx, swa, W: int, q_pos0: int, *,
     ws = _workspace(L.csa2_sparse_attn_prefill_workspace_size(ctypes.byref(a)), q.device)
     _check(L.csa2_sparse_attn_prefill(ctypes.byref(a), _ptr(ws), 0 if ws is None else ws.numel(),
                                       _stream(stream)))
+    return out
+
+
+def csa2_prefill_topk(q_idx, w, k_idx, ctx_len: int, q_pos0: int, m: int, k: int, *, out=None,
+                      workspace=None, stream=None):
+    """Full-mode top-k of a prefill chunk.  q_idx [T][8][128] bf16, w [T][8]
+    f32, k_idx one sequence's tiled indexer cache [cap][128] (or [1][cap][128])
+    bf16; query t sits at position q_pos0 + t.  Returns out [T][k] int32."""
+    for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
+        _dev(t, nm)
+    T, H_I, d_I = q_idx.shape
+    kc = k_idx.reshape(-1, k_idx.shape[-1])
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=q_idx.device)
+    a = PrefillTopkArgs(q_idx=q_idx.data_ptr(), q_dtype=_dtype(q_idx, "q_idx"), w=w.data_ptr(),
+                        k_idx=kc.data_ptr(), k_dtype=_dtype(kc, "k_idx"), T=T, cap=kc.shape[0], H_I=H_I,
+                        d_I=d_I, ctx_len=int(ctx_len), q_pos0=int(q_pos0), m=int(m), k=int(k),
+                        out_idx=out.data_ptr())
+    L = lib()
+    need = L.csa2_prefill_topk_workspace_size(ctypes.byref(a))
+    ws = workspace if workspace is not None else _workspace(need, q_idx.device)
+    _check(L.csa2_prefill_topk(ctypes.byref(a), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream)))
     return out

@@ -261,3 +261,53 @@ int csa2_sparse_attn_prefill(const csa2_attn_prefill_args* a, void* ws, size_t w
 }
 
 }  // extern "C"
+
+// --------------------------------------------------------------------------
+namespace {
+int check_prefill_topk(const csa2_prefill_topk_args* a) {
+    const char* fn = "csa2_prefill_topk";
+    if (!a) return fail(CSA2_E_INVALID, "%s: args is null", fn);
+    if (a->T < 0) return fail(CSA2_E_INVALID, "%s: T < 0", fn);
+    if (a->cap < 0 || a->cap % 64 != 0) return fail(CSA2_E_INVALID, "%s: cap=%lld must be a multiple of 64", fn,
+                                                    static_cast<long long>(a->cap));
+    if (a->ctx_len < 0 || a->ctx_len > a->cap) return fail(CSA2_E_INVALID, "%s: ctx_len outside [0, cap]", fn);
+    if (a->m < 1) return fail(CSA2_E_INVALID, "%s: m must be >= 1", fn);
+    if (a->q_pos0 < 0) return fail(CSA2_E_INVALID, "%s: q_pos0 < 0", fn);
+    if (a->k < 1) return fail(CSA2_E_INVALID, "%s: k must be >= 1", fn);
+    if (!valid_dtype(a->q_dtype) || !valid_dtype(a->k_dtype)) return fail(CSA2_E_INVALID, "%s: bad dtype", fn);
+    if (a->q_dtype != CSA2_BF16 || a->k_dtype != CSA2_BF16)
+        return fail(CSA2_E_UNSUPPORTED, "%s: q and k must be bf16", fn);
+    if (a->H_I != 8 || a->d_I != 128)
+        return fail(CSA2_E_UNSUPPORTED, "%s: H_I=%d d_I=%d (8 x 128 only)", fn, a->H_I, a->d_I);
+    if (a->k > csa2::prefill_topk_max_k())
+        return fail(CSA2_E_UNSUPPORTED, "%s: k=%d above %d", fn, a->k, csa2::prefill_topk_max_k());
+    if (a->T > 0 && (!a->q_idx || !a->w || !a->out_idx || (a->ctx_len > 0 && !a->k_idx)))
+        return fail(CSA2_E_INVALID, "%s: null tensor", fn);
+    if (!aligned(a->q_idx, 16) || !aligned(a->k_idx, 16))
+        return fail(CSA2_E_INVALID, "%s: q_idx and k_idx must be 16-byte aligned", fn);
+    return CSA2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t csa2_prefill_topk_workspace_size(const csa2_prefill_topk_args* a) {
+    if (check_prefill_topk(a) != CSA2_OK) return 0;
+    return csa2::prefill_topk_workspace_bytes(a->T, a->ctx_len, a->q_pos0, a->m);
+}
+
+int csa2_prefill_topk(const csa2_prefill_topk_args* a, void* ws, size_t ws_bytes, void* stream) {
+    const int rc = check_prefill_topk(a);
+    if (rc != CSA2_OK) return rc;
+    if (a->T == 0) return ok();
+    const size_t need = csa2::prefill_topk_workspace_bytes(a->T, a->ctx_len, a->q_pos0, a->m);
+    if (!ws || ws_bytes < need)
+        return fail(CSA2_E_WORKSPACE, "csa2_prefill_topk: workspace %zu bytes < required %zu", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(CSA2_E_INVALID, "csa2_prefill_topk: workspace must be 256-byte aligned");
+    csa2::PrefillLaunch L;
+    L.q = a->q_idx; L.w = a->w; L.k_idx = a->k_idx; L.T = a->T; L.cap = a->cap; L.ctx_len = a->ctx_len;
+    L.q_pos0 = a->q_pos0; L.m = a->m; L.k = a->k; L.out = a->out_idx;
+    return device_status(csa2::launch_prefill_topk(L, ws, as_stream(stream)), "csa2_prefill_topk");
+}
+
+}  // extern "C"

@@ -60,4 +60,21 @@ bool attn_shape_supported(int H, int D);
 size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W);
 hipError_t launch_attn(const AttnLaunch& p, hipStream_t st);
 
+
+// ---- prefill Full-mode top-k (matrix-core scores, exact band)
+struct PrefillLaunch {
+    const void* q;          // [T][8][128] bf16
+    const float* w;         // [T][8]
+    const void* k_idx;      // tiled bf16 indexer cache, cap rows
+    int64_t T, cap;
+    int32_t ctx_len;
+    int64_t q_pos0;
+    int32_t m;
+    int32_t k;
+    int32_t* out;           // [T][k]
+};
+size_t prefill_topk_workspace_bytes(int64_t T, int32_t ctx_len, int64_t q_pos0, int32_t m);
+int prefill_topk_max_k();
+hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st);
+
 }  // namespace csa2

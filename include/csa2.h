@@ -241,6 +241,44 @@ size_t csa2_sparse_attn_prefill_workspace_size(const csa2_attn_prefill_args *a);
 int csa2_sparse_attn_prefill(const csa2_attn_prefill_args *a, void *ws, size_t ws_bytes,
                              void *stream);
 
+
+/* ------------------------------------------------------------------------
+ * csa2_prefill_topk - Full-mode top-k indices for a chunk of prefill query
+ * tokens ([KVC] sections 1-2: encoder Full layers score every visible
+ * entry; [KVC] section 2 for m-token entries).  The result is identical to
+ * csa2_index_score (q_pos = q_pos0 + t, Tq = T, B = 1) followed by csa2_topk
+ * with k: the same exact scores, the same (score desc, position asc) order.
+ * The scores are formed on the matrix cores; keys whose approximate score
+ * lies within a proven error band of the k-th are rescored with the exact
+ * float32 chains, so no index differs.
+ *
+ * Query t (0 <= t < T) sits at absolute token position q_pos0 + t and sees
+ * vis(t) = min(ctx_len, floor((q_pos0 + t + 1) / m)) entries.
+ *   q_idx  [T][H_I][d_I] bf16, w [T][H_I] f32   (H_I = 8, d_I = 128 only)
+ *   k_idx  one sequence's indexer cache, tiled layout (csa2_index_score),
+ *          cap rows (cap % 64 == 0), bf16
+ *   out_idx [T][k] int32: min(k, vis(t)) ascending positions, then -1.
+ * 1 <= k <= 4096.  Inputs must be finite with scores far from float32
+ * overflow.  Workspace: csa2_prefill_topk_workspace_size (about
+ * 4 * min(T, 1024) * vis(T-1) bytes of approximate scores plus 100 KB per
+ * row of that chunk); 256-byte aligned.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_prefill_topk_args {
+    const void *q_idx;  int32_t q_dtype;  /* [T][H_I][d_I] */
+    const float *w;                       /* [T][H_I] */
+    const void *k_idx;  int32_t k_dtype;  /* cap rows, tiled layout */
+    int64_t T, cap;
+    int32_t H_I, d_I;
+    int32_t ctx_len;
+    int64_t q_pos0;
+    int32_t m;
+    int32_t k;
+    int32_t *out_idx;                     /* [T][k] */
+} csa2_prefill_topk_args;
+
+size_t csa2_prefill_topk_workspace_size(const csa2_prefill_topk_args *a);
+int csa2_prefill_topk(const csa2_prefill_topk_args *a, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

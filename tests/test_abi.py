@@ -87,3 +87,29 @@ def test_kv_write_and_attention_argument_checks():
     assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 2
     a.H, a.D = 64, 40
     assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 1
+
+
+def test_prefill_topk_argument_checks():
+    L = binding.lib()
+    a = binding.PrefillTopkArgs(q_idx=256, q_dtype=1, w=256, k_idx=256, k_dtype=1, T=16, cap=1024, H_I=8,
+                                d_I=128, ctx_len=1000, q_pos0=1990, m=2, k=64, out_idx=256)
+    need = L.csa2_prefill_topk_workspace_size(ctypes.byref(a))
+    assert need > 16 * 1000 * 4                      # approximate score rows of the chunk
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 3
+    assert "workspace" in _err()
+    a.H_I = 4
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 2
+    assert L.csa2_prefill_topk_workspace_size(ctypes.byref(a)) == 0
+    a.H_I, a.q_dtype = 8, 0
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 2
+    a.q_dtype, a.k = 1, 5000
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 2
+    a.k, a.cap = 64, 1000
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 1
+    assert "multiple of 64" in _err()
+    a.cap, a.m = 1024, 0
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 1
+    a.m, a.ctx_len = 2, 2000
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 1
+    a.ctx_len, a.T = 1000, 0
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 0    # nothing to do
