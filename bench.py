@@ -36,6 +36,7 @@ import torch  # noqa: E402
 import csa2_inputs as ci  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16/fp16 matrix peak, vendor figure
 METRIC = "CSA2 decode queries/s & achieved HBM GB/s at 128K and 1M ctx (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_scan_traffic.json")
 
@@ -192,6 +193,62 @@ def run_workload(K, w: ci.Workload, steps: int, warmup: int, dev, n_sets: int = 
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     return dict(sets=sets, runners=runners, ms_per_step=ms_step, wall_s=wall, scan_ms=scan_ms,
                 scan_name=scan_name)
+
+
+def run_prefill(K, w: ci.Workload, steps: int, warmup: int, dev):
+    """The encoder prefill chunk: T query tokens at positions prior..prior+T-1
+    (m tokens per entry), the chunk's T/m new entries written, the Full
+    layer's per-token top-k over the visible entries, and attention for every
+    layer of the schedule.  One input set (a step moves several GB)."""
+    from compressed_sparse_attention_05_amd.prefill import PrefillChunk, PrefillLayer
+    seed, N, D, d_I, T, m, W, H = w.seed, w.N, w.D, w.d_I, w.T, w.m, w.W, w.H
+    n_prior = w.prior_tokens // m
+    codes = torch.empty((1, N, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((1, N, D // 16), dtype=torch.uint8, device=dev)
+    fill_kv_cache(K, codes, scales, seed, n_prior, D)
+    rows = torch.empty((1, N, d_I), dtype=torch.bfloat16, device=dev)
+    ci.fill_gaussian_(rows, seed, ci.TID_K_IDX)
+    k_idx = K.tile_indexer_cache(rows)[0]
+    del rows
+    dst = torch.arange(n_prior, N, device=dev, dtype=torch.int64)
+    new_kv = ci.gaussian_rows(seed, ci.TID_KV, dst, D, dtype=torch.bfloat16, clip=ci.NORM_BOUND)
+    new_kidx = ci.gaussian_rows(seed, ci.TID_K_IDX, dst, d_I, dtype=torch.bfloat16)
+    layers = []
+    for li, mode in enumerate(w.schedule):
+        lay = PrefillLayer(q=ci.gaussian(seed, ci.layer_tid(ci.TID_Q, li), (T, H, D), torch.bfloat16, dev),
+                           swa=ci.gaussian(seed, ci.layer_tid(ci.TID_SWA, li), (T + W - 1, D), torch.bfloat16, dev))
+        if mode == "F":
+            lay.q_idx = ci.gaussian(seed, ci.layer_tid(ci.TID_Q_IDX, li), (T, w.H_I, d_I), torch.bfloat16, dev)
+            lay.w = ci.uniform(seed, ci.layer_tid(ci.TID_W, li), (T, w.H_I), dev)
+        layers.append(lay)
+    chunk = PrefillChunk(w.schedule, codes[0], scales[0], k_idx, N, w.prior_tokens, m, w.k, W, layers,
+                         new_kv=new_kv, new_kidx=new_kidx, dst_row=dst)
+    for _ in range(warmup):
+        chunk.run()
+    torch.cuda.synchronize()
+    names = ["topk"] + [f"attn{i}" for i in range(len(w.schedule))]
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        chunk.run(events=evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    topk_ms = sum(e["topk"][0].elapsed_time(e["topk"][1]) for e in evs) / steps
+    attn_ms = sum(e[n][0].elapsed_time(e[n][1]) for e in evs for n in names[1:]) / steps
+    pairs = sum(min(N, (w.prior_tokens + t + 1) // m) for t in range(T))
+    score_flop = pairs * w.H_I * d_I * 2
+    attn_flop = len(w.schedule) * T * w.H * (w.k + W) * D * 2 * 2
+    return {"workload": w.name, "tokens": T, "context": N, "schedule": w.schedule,
+            "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 3),
+            "topk_ms": round(topk_ms, 3),
+            "topk_scoring_TFLOPs": round(score_flop / (topk_ms * 1e-3) / 1e12, 1),
+            "topk_mfma_frac": round(score_flop / (topk_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attn_ms": round(attn_ms, 3),
+            "attn_TFLOPs": round(attn_flop / (attn_ms * 1e-3) / 1e12, 1),
+            "attn_mfma_frac": round(attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
@@ -368,6 +425,10 @@ def main(argv=None):
                         "hbm_frac": round(alg2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "scan": {"kernel": r["scan_name"], "us": round(r["scan_ms"] * 1e3, 2),
                                  "GBps": round(scan_b / (r["scan_ms"] * 1e-3) / 1e9, 1)}})
+        del r
+        torch.cuda.empty_cache()
+        print(f"# setting up {ci.PREFILL_CHUNK.name}", file=sys.stderr, flush=True)
+        sec.append(run_prefill(K, ci.PREFILL_CHUNK, 3, 1, dev))
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
     return 0
