@@ -8,23 +8,23 @@
 //     out_h = softmax_j(sm_scale * q_h . row_j) . rows
 // The latent (D channels) is both key and value; all heads share the rows.
 //
-// Work split: one workgroup = (unit, key split, block of 64 heads), 2*NQ
-// waves (8 at D = 512).  Wave w owns head group hg = w & 1 (32 heads) and
-// channel slice dq = w >> 1 (D/NQ channels).  Keys stream in tiles of 32:
-//  1. all threads gather the tile's rows (prefetched one tile ahead) and
-//     dequantise them to fp16 into LDS twice: key-major Kt[key][d] (for S)
-//     and Vt[step][grp][cell(d)][8 keys] (for P.V, so every MFMA operand is
-//     one 16-byte LDS read; cell() is a bank swizzle);
-//  2. S^T[key][head] over this wave's channel slice with
-//     v_mfma_f32_32x32x16_f16 (A = key rows, B = q in registers), then the
-//     NQ slices are added through LDS (same order in every wave);
-//  3. online softmax in base 2: each lane holds one head's 16 keys and its
-//     partner lane (l ^ 32) the other 16, so the statistics need one
-//     cross-lane max per tile;
-//  4. O^T[d][head] += V^T P^T with the fp16-rounded probabilities taken
-//     straight from the S accumulators: the MFMA k-slot order is chosen to
-//     be the accumulator row order, so no shuffle is needed.  The running
-//     sum uses the same rounded probabilities.
+// Two kernels share the tile scheme (keys stream through LDS in tiles, the
+// dequantised tile is stored once key-major, and P.V reads it transposed
+// with ds_read_b64_tr_b16):
+//  * attn_kernel<D, NQ> (few query units; also D = 64): one workgroup =
+//    (unit, key split, block of 64 heads), 2*NQ waves; wave w owns head group
+//    hg = w & 1 and channel slice dq = w >> 1.  Per tile all waves gather and
+//    dequantise, form S^T over their channel slice (the NQ slices added
+//    through LDS), run the online softmax and add V^T P^T for their slice;
+//  * attn_ws_kernel (D = 512, many units): warp-specialised, see there.
+// Common to both:
+//  - S^T[key][head] with v_mfma_f32_32x32x16_f16 (A = key rows, B = q);
+//  - online softmax in base 2 with a lazy reference: p = exp2(t - m_ref),
+//    m_ref moves (and O, l are rescaled) only when a tile max exceeds it by
+//    more than 8, so p < 2^8; the final division uses the same reference;
+//  - O^T[d][head] += V^T P^T with the fp16-rounded probabilities taken
+//    straight from the S accumulators (the MFMA k-slot order is chosen to be
+//    the accumulator row order); the running sum uses the same rounded p.
 // Partial results of several key splits are merged by combine_kernel.
 //
 // Exactness: every MXFP4 value is an fp16 number (E2M1 times E4M3 has at
@@ -38,9 +38,10 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kKT = 32;          // keys per tile
 constexpr int kMaxTilesPerSplit = 16;
 constexpr int kCombineMaxSplits = 64;  // key splits one combine block can merge
 constexpr float kLog2e = 1.4426950408889634f;
@@ -64,31 +65,27 @@ __device__ __forceinline__ uint32_t f16_bits(float v) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
 }
 
-// Non-negative finite E4M3 code -> float (exact).
-__device__ __forceinline__ float e4m3_val(uint32_t c) {
-    return (c < 8u) ? static_cast<float>(c) * 0x1p-9f
-                    : __uint_as_float((c << 20) + (120u << 23));
-}
-
 // 8 MXFP4 nibbles (channels 0..7 of a code dword, channel 2i in the low
-// nibble of byte i) times an fp16 scale -> 4 dwords of packed fp16 pairs
-// (channel 2p low half, 2p+1 high half).  E2M1 magnitudes have a zero low
-// byte in fp16, so a byte permute over the table of high bytes
-// {00,38,3C,3E,40,42,44,46} does the lookup.
-__device__ __forceinline__ void dequant8(uint32_t cw, uint32_t scale_h2, uint32_t out[4]) {
-    const uint32_t tlo = 0x3E3C3800u, thi = 0x46444240u;
-    const uint32_t hb_lo = __builtin_amdgcn_perm(thi, tlo, cw & 0x07070707u) |
-                           ((cw & 0x08080808u) << 4);                 // channels 0,2,4,6
-    const uint32_t hb_hi = __builtin_amdgcn_perm(thi, tlo, (cw >> 4) & 0x07070707u) |
-                           (cw & 0x80808080u);                        // channels 1,3,5,7
-    const half2v s = __builtin_bit_cast(half2v, scale_h2);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t sel = 0x0Cu | (static_cast<uint32_t>(p) << 8) | (0x0Cu << 16) |
-                             (static_cast<uint32_t>(4 + p) << 24);
-        const uint32_t pair = __builtin_amdgcn_perm(hb_hi, hb_lo, sel);
-        out[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pair) * s);
-    }
+// nibble of byte i) times their E4M3 scale -> 4 dwords of packed fp16 pairs
+// (channel 2p low half, 2p+1 high half), with the gfx950 converters: E2M1
+// pairs to fp16 at unit scale (the converter applies only the exponent of its
+// scale, so the E4M3 scale is a separate fp16 multiply) and the E4M3 scale
+// byte to an fp16 pair.  Every step is exact: E2M1 times E4M3 has at most 5
+// significant bits within fp16 range.  The scale code is clamped to 0x7e: an
+// unwritten row's 0x7f (NaN in E4M3) must stay finite, since its zero weight
+// only cancels finite values.
+__device__ __forceinline__ void dequant8_hw(uint32_t cw, uint32_t sc, uint32_t out[4]) {
+    uint32_t c = sc & 0x7fu;
+    c = c < 0x7eu ? c : 0x7eu;
+    const half2v s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c | (c << 8), 1.0f, false);
+    const half2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0);
+    const half2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1);
+    const half2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2);
+    const half2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3);
+    out[0] = __builtin_bit_cast(uint32_t, v0 * s);
+    out[1] = __builtin_bit_cast(uint32_t, v1 * s);
+    out[2] = __builtin_bit_cast(uint32_t, v2 * s);
+    out[3] = __builtin_bit_cast(uint32_t, v3 * s);
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -107,21 +104,18 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
     constexpr int MT = DQ / 32;            // O^T row tiles per wave
     constexpr int KROW = D + 8;            // padded Kt row (halves)
     constexpr int CH = D / 8;              // 8-channel chunks per row
-    constexpr int KPT = kKT / NW;          // keys dequantised per thread
-    static_assert(DQ % 32 == 0 && (KPT == 4 || KPT == 8), "unsupported split");
-    // Kt is dead once S is formed, so the S partials ([NW][16][64] float32)
-    // reuse its space.
-    constexpr int KT_BYTES = kKT * KROW * 2;
-    constexpr int SP_BYTES = NW * 16 * 64 * 4;
-    constexpr int KBUF = KT_BYTES > SP_BYTES ? KT_BYTES : SP_BYTES;
-    __shared__ __attribute__((aligned(16))) unsigned char kbuf[KBUF];
-    __shared__ __attribute__((aligned(16))) _Float16 Vt[kKT * D];
+    constexpr int KT = 8 * NW;             // keys per tile (64 at D = 512)
+    constexpr int KPT = 8;                 // keys dequantised per thread
+    constexpr int MK = KT / 32;            // 32-key row blocks of S^T per tile
+    static_assert(DQ % 32 == 0, "unsupported split");
+    // Kt holds the tile once, key-major; P.V reads it transposed
+    // (ds_read_b64_tr_b16), so there is no second copy.
+    __shared__ __attribute__((aligned(16))) _Float16 Kt[KT * KROW];
+    __shared__ __attribute__((aligned(16))) float Spart[NW * MK * 16 * 64];
     // 0 for a key that holds a row, -inf for an empty slot: added to the
     // logits, so empty slots get probability exactly 0 without a branch
-    __shared__ __attribute__((aligned(16))) float kmask[kKT];
-    __shared__ int32_t idx_s[kKT * kMaxTilesPerSplit];
-    _Float16* Kt = reinterpret_cast<_Float16*>(kbuf);
-    float* Spart = reinterpret_cast<float*>(kbuf);
+    __shared__ __attribute__((aligned(16))) float kmask[KT];
+    __shared__ int32_t idx_s[KT * kMaxTilesPerSplit];
 
     // the wave index is uniform within a wave: make that explicit so every
     // decision derived from it (key slot, channel slice) is a scalar branch
@@ -211,8 +205,8 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
     int win0 = t_begin;
     auto stage_idx = [&](int first_tile) {
         win0 = first_tile;
-        for (int i = tid; i < kMaxTilesPerSplit * kKT; i += NT) {
-            const int slot = first_tile * kKT + i;
+        for (int i = tid; i < kMaxTilesPerSplit * KT; i += NT) {
+            const int slot = first_tile * KT + i;
             idx_s[i] = slot < a.k ? idx[slot] : -1;
         }
     };
@@ -222,8 +216,8 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
     // dequant role: this wave covers KPT keys of the 8-key group g8 (step
     // sg = g8 >> 1, group gg = g8 & 1), slots i8 = i + 8 - ... of that group;
     // lane j handles channels 8j..8j+7.
-    const int g8 = KPT == 8 ? wv : (wv >> 1);
-    const int half = KPT == 8 ? 0 : (wv & 1);
+    const int g8 = wv;
+    const int half = 0;
     const int sg = g8 >> 1, gg = g8 & 1;
     const int j = lane;
     auto key_of_i = [&](int i) {
@@ -245,9 +239,9 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
     auto load_raw = [&](int tile) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int slot = tile * kKT + key_of_i(i);
+            const int slot = tile * KT + key_of_i(i);
             if (slot < a.k) {
-                const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * kKT]);
+                const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * KT]);
                 const bool ok = row >= 0 && row < a.cap;
                 const int64_t rr = kvbase + (ok ? row : 0);
                 raw_kind[i] = ok ? 1 : 0;
@@ -270,13 +264,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
         }
     };
 
-    // Vt cell of channel d: the low three bits are XORed with the next three,
-    // so the dequantising lanes (channels 8j + c for lanes j) spread over all
-    // banks instead of landing 128 bytes apart, while any 8 consecutive
-    // channels read by the P.V operand still fill 8 distinct cells.
-    auto vcell = [](int d) { return d ^ ((d >> 3) & 7); };
-
-    // dequantise this thread's KPT keys (values in h) into Kt and Vt
+    // dequantised KPT keys of this thread (values in h) into Kt
     auto store_tile = [&](const uint32_t (&h)[KPT][4], const int (&kind)[KPT]) {
         if (j < CH) {
 #pragma unroll
@@ -286,82 +274,64 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
                 *reinterpret_cast<uint4*>(&Kt[key * KROW + 8 * j]) =
                     make_uint4(h[i][0], h[i][1], h[i][2], h[i][3]);
             }
-            // transpose KPT keys x 8 channels into Vt[sg][gg][d][slot i8]
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t lo4[KPT / 2], hi4[KPT / 2];
-#pragma unroll
-                for (int q = 0; q < KPT / 2; ++q) {
-                    lo4[q] = __builtin_amdgcn_perm(h[2 * q + 1][p], h[2 * q][p], 0x05040100u);
-                    hi4[q] = __builtin_amdgcn_perm(h[2 * q + 1][p], h[2 * q][p], 0x07060302u);
-                }
-                const int grp = (sg * 2 + gg) * D;
-                _Float16* lo_p = &Vt[(grp + vcell(8 * j + 2 * p)) * 8 + 4 * half];
-                _Float16* hi_p = &Vt[(grp + vcell(8 * j + 2 * p + 1)) * 8 + 4 * half];
-                if (KPT == 8) {
-                    *reinterpret_cast<uint4*>(lo_p) = make_uint4(lo4[0], lo4[1], lo4[KPT / 2 - 2], lo4[KPT / 2 - 1]);
-                    *reinterpret_cast<uint4*>(hi_p) = make_uint4(hi4[0], hi4[1], hi4[KPT / 2 - 2], hi4[KPT / 2 - 1]);
-                } else {
-                    *reinterpret_cast<uint2*>(lo_p) = make_uint2(lo4[0], lo4[KPT / 2 - 1]);
-                    *reinterpret_cast<uint2*>(hi_p) = make_uint2(hi4[0], hi4[KPT / 2 - 1]);
-                }
-            }
         }
     };
 
-    // S, online softmax and P.V for the tile currently in Kt/Vt
+    // S, online softmax and P.V for the tile currently in Kt
     auto tile_math = [&]() {
-        // ---------------- 2. S^T partial over this wave's channel slice
-        floatx16 s_acc;
+        // ---------------- 2. S^T partial over this wave's channel slice, one
+        // 32-key row block at a time
+        floatx16 s_acc[MK];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s_acc[r] = 0.0f;
+        for (int mk = 0; mk < MK; ++mk) {
 #pragma unroll
-        for (int st = 0; st < SSTEPS; ++st) {
-            const int d0 = dq * DQ + 16 * st + 8 * (lane >> 5);
-            const half8 kf = *reinterpret_cast<const half8*>(&Kt[(lane & 31) * KROW + d0]);
-            s_acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s_acc, 0, 0, 0);
-        }
-        float kmk[16];
-        {
-            const float4* km4 = reinterpret_cast<const float4*>(kmask);
+            for (int r = 0; r < 16; ++r) s_acc[mk][r] = 0.0f;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                // rows 8*r4 + 4*(lane/32) + 0..3
-                const float4 v = km4[2 * r4 + (lane >> 5)];
-                kmk[4 * r4] = v.x; kmk[4 * r4 + 1] = v.y; kmk[4 * r4 + 2] = v.z; kmk[4 * r4 + 3] = v.w;
+            for (int st = 0; st < SSTEPS; ++st) {
+                const int d0 = dq * DQ + 16 * st + 8 * (lane >> 5);
+                const half8 kf = *reinterpret_cast<const half8*>(&Kt[(32 * mk + (lane & 31)) * KROW + d0]);
+                s_acc[mk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s_acc[mk], 0, 0, 0);
             }
         }
-        __syncthreads();   // everyone done reading Kt before Spart overwrites it
-        // partials as [wave][r/4][lane][4]: one 16-byte LDS access per 4 rows
+        // partials as [wave][mk][r/4][lane][4]: one 16-byte LDS access per 4 rows
         float4* Sp4 = reinterpret_cast<float4*>(Spart);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            Sp4[(wv * 4 + r4) * 64 + lane] = make_float4(s_acc[4 * r4], s_acc[4 * r4 + 1],
-                                                         s_acc[4 * r4 + 2], s_acc[4 * r4 + 3]);
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                Sp4[((wv * MK + mk) * 4 + r4) * 64 + lane] =
+                    make_float4(s_acc[mk][4 * r4], s_acc[mk][4 * r4 + 1], s_acc[mk][4 * r4 + 2], s_acc[mk][4 * r4 + 3]);
         __syncthreads();
-        float t2[16];
+        float t2[MK][16];
+        const float4* km4 = reinterpret_cast<const float4*>(kmask);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            float4 sum = Sp4[(hg * 4 + r4) * 64 + lane];
+        for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int qq = 1; qq < NQ; ++qq) {
-                const float4 v = Sp4[((hg + 2 * qq) * 4 + r4) * 64 + lane];
-                sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float4 sum = Sp4[((hg * MK + mk) * 4 + r4) * 64 + lane];
+#pragma unroll
+                for (int qq = 1; qq < NQ; ++qq) {
+                    const float4 v = Sp4[(((hg + 2 * qq) * MK + mk) * 4 + r4) * 64 + lane];
+                    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+                }
+                // rows 32*mk + 8*r4 + 4*(lane/32) + 0..3
+                const float4 km = km4[8 * mk + 2 * r4 + (lane >> 5)];
+                t2[mk][4 * r4] = fmaf(sum.x, a.c2, km.x);
+                t2[mk][4 * r4 + 1] = fmaf(sum.y, a.c2, km.y);
+                t2[mk][4 * r4 + 2] = fmaf(sum.z, a.c2, km.z);
+                t2[mk][4 * r4 + 3] = fmaf(sum.w, a.c2, km.w);
             }
-            t2[4 * r4] = fmaf(sum.x, a.c2, kmk[4 * r4]);
-            t2[4 * r4 + 1] = fmaf(sum.y, a.c2, kmk[4 * r4 + 1]);
-            t2[4 * r4 + 2] = fmaf(sum.z, a.c2, kmk[4 * r4 + 2]);
-            t2[4 * r4 + 3] = fmaf(sum.w, a.c2, kmk[4 * r4 + 3]);
-        }
 
         // ---------------- 3. online softmax (base 2) with a lazy reference:
         // probabilities are exp2(t - m_ref); m_ref moves (and O, l are
         // rescaled) only when some lane's tile max exceeds it by more than 8,
         // so p stays below 2^8 and the rescale is rare.  The final division
         // by l uses the same reference, so the result does not depend on it.
-        float tmax = t2[0];
+        float tmax = t2[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, t2[r]);
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, t2[mk][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const bool grow = tmax > m_run + 8.0f || (m_run == -__builtin_inff() && tmax != -__builtin_inff());
         if (__ballot(grow) != 0) {
@@ -376,33 +346,50 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
             }
             m_run = m_new;
         }
-        uint32_t pk[8];
+        uint32_t pk[MK][8];
         float psum = 0.0f;
         if (m_run == -__builtin_inff()) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) pk[q] = 0u;
+            for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) pk[mk][q] = 0u;
         } else {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                // v_exp_f32 directly: arguments are <= 8, and results too
-                // small for fp16 become 0 either way
-                const half2v ph = {static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[2 * q] - m_run)),
-                                   static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[2 * q + 1] - m_run))};
-                psum = __builtin_amdgcn_fdot2(ph, half2v{1.0f16, 1.0f16}, psum, false);
-                pk[q] = __builtin_bit_cast(uint32_t, ph);
-            }
+            for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    // v_exp_f32 directly: arguments are <= 8, and results too
+                    // small for fp16 become 0 either way
+                    const half2v ph = {static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[mk][2 * q] - m_run)),
+                                       static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[mk][2 * q + 1] - m_run))};
+                    psum = __builtin_amdgcn_fdot2(ph, half2v{1.0f16, 1.0f16}, psum, false);
+                    pk[mk][q] = __builtin_bit_cast(uint32_t, ph);
+                }
         }
         l_run += psum;
 
         // ---------------- 4. O^T += V^T P^T over this wave's channel slice
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const half8 pf = __builtin_bit_cast(half8, make_uint4(pk[4 * ks], pk[4 * ks + 1],
-                                                                  pk[4 * ks + 2], pk[4 * ks + 3]));
+        for (int ks = 0; ks < 2 * MK; ++ks) {
+            const uint32_t* pp = &pk[ks >> 1][4 * (ks & 1)];
+            const half8 pf = __builtin_bit_cast(half8, make_uint4(pp[0], pp[1], pp[2], pp[3]));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int d = dq * DQ + 32 * mt + (lane & 31);
-                const half8 vf = *reinterpret_cast<const half8*>(&Vt[((ks * 2 + (lane >> 5)) * D + vcell(d)) * 8]);
+                // A = V^T[32 d][16 k-slots]; k-slot 8h + i holds key
+                // 16ks + 4h + (i % 4) + 8(i / 4) (h = lane / 32), the order of
+                // the P fragment.  In each 16-lane group g the transposed read
+                // hands lane 16g + i' the elements i' % 4 of lanes 4e + i'/4
+                // (e = 0..3), so lane 16g + j reads 4 channels of key
+                // 16ks + 4(g/2) + j/4 (then 8 keys further for i >= 4).
+                const int g = lane >> 4, j = lane & 15;
+                const int key = 16 * ks + 4 * (g >> 1) + (j >> 2);
+                const int d = dq * DQ + 32 * mt + 16 * (g & 1) + 4 * (j & 3);
+                const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4v __attribute__((address_space(3)))*)(&Kt[key * KROW + d]));
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4v __attribute__((address_space(3)))*)(&Kt[(key + 8) * KROW + d]));
+                const short8v vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                const half8 vf = __builtin_bit_cast(half8, vv);
                 o_acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o_acc[mt], 0, 0, 0);
             }
         }
@@ -410,14 +397,14 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
 
     // ---- main tiles (every slot a main-KV slot): branch-free gathers
     // prefetched one tile ahead into registers no other path writes
-    const int t_main_end = (a.k / kKT) < t_end ? (a.k / kKT) : t_end;
+    const int t_main_end = (a.k / KT) < t_end ? (a.k / KT) : t_end;
     uint32_t pm_cw[KPT], pm_sc[KPT];
     int pm_ok[KPT];
     auto load_main = [&](int tile) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int slot = tile * kKT + key_of_i(i);
-            const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * kKT]);
+            const int slot = tile * KT + key_of_i(i);
+            const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * KT]);
             const bool ok = row >= 0 && row < a.cap;
             const int64_t rr = kvbase + (ok ? row : 0);
             pm_ok[i] = ok;
@@ -432,8 +419,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
             int kind[KPT];
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
-                const uint32_t s16 = f16_bits(e4m3_val(pm_sc[i] & 0x7fu));
-                dequant8(pm_cw[i], s16 | (s16 << 16), h[i]);
+                dequant8_hw(pm_cw[i], pm_sc[i], h[i]);
                 // an empty slot keeps the (finite) values of the clamped row:
                 // its logit is -inf, so it enters P.V with weight exactly 0
                 kind[i] = pm_ok[i] ? 1 : 0;
@@ -465,8 +451,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
                 if (raw_kind[i] == 1) {
-                    const uint32_t s16 = f16_bits(e4m3_val(raw_sc[i] & 0x7fu));
-                    dequant8(raw_cw[i], s16 | (s16 << 16), h[i]);
+                    dequant8_hw(raw_cw[i], raw_sc[i], h[i]);
                 } else if (raw_kind[i] == 2) {
                     if (BF16) {
 #pragma unroll
@@ -518,6 +503,381 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
         if (dq == 0 && lane < 32) {
             a.ws_m[pidx * 64 + head_local] = m_run;
             a.ws_l[pidx * 64 + head_local] = l_tot;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// D = 512: warp-specialised tiles of 64 keys.  Eight waves in two roles:
+//   S-waves 0..3 (head group hg = w & 1, key block kb = w >> 1): S^T for 32
+//     keys x 32 heads over all 512 channels (32 MFMAs, q in registers), the
+//     online softmax of that block and its P fragments;
+//   D-waves 4..7 (channel slice dw = w - 4): gather and dequantise the next
+//     tile into the other Kt buffer (16 keys each), and O^T[128 d][64 heads]
+//     += V^T P^T with V^T read transposed from Kt.
+// Per tile two phases separated by barriers:
+//   phase 1: S-waves S(i) and their block max   || D-waves P.V(i - 1)
+//   phase 2: S-waves softmax(i) -> P, rescale   || D-waves dequant(i + 1)
+// so the matrix cores of every SIMD get work from both roles and no S
+// partial sums cross waves (each S-wave covers all channels).
+template <bool BF16>
+__global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
+    constexpr int D = 512, KT = 64, KROW = D + 8, SSTEPS = D / 16;
+    __shared__ __attribute__((aligned(16))) _Float16 Kt[2][KT * KROW];
+    __shared__ __attribute__((aligned(16))) uint4 Pb[2][4][64];   // [head group][k-step][lane]
+    __shared__ __attribute__((aligned(16))) float kmask[2][KT];
+    __shared__ float Lm[2][2][32];                                 // block max [hg][kb][head]
+    __shared__ float alpha_s[64];
+    __shared__ int grow_s[2];
+    __shared__ float Lsum[2][2][32];
+    __shared__ float Mfin[64];
+    __shared__ int32_t idx_s[KT * kMaxTilesPerSplit];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool s_role = wv < 4;
+    const int hg = wv & 1, kb = (wv >> 1) & 1;
+    const int dw = wv & 3;
+    const int64_t u = blockIdx.x;
+    const int split = blockIdx.y;
+    const int hb = blockIdx.z;
+    const int hbase = hb * 64;
+
+    // ---- unit geometry
+    const int32_t* idx = a.idx + u * a.k;
+    const int64_t kvbase = u * a.kv_unit_stride;
+    const uint8_t* swa_rows;
+    int n_swa;
+    const int64_t swa_row_bytes = static_cast<int64_t>(D) * (BF16 ? 2 : 4);
+    if (a.prefill) {
+        const int64_t i = a.q_pos0 + u;
+        int64_t lo = i - a.W + 1;
+        if (lo < a.swa_start) lo = a.swa_start;
+        if (lo < 0) lo = 0;
+        n_swa = static_cast<int>(i - lo + 1 > 0 ? i - lo + 1 : 0);
+        swa_rows = a.swa + (lo - (a.q_pos0 - (a.W - 1))) * swa_row_bytes;
+    } else {
+        int sl = a.swa_len[u];
+        n_swa = sl < a.W ? (sl > 0 ? sl : 0) : a.W;
+        swa_rows = a.swa + u * static_cast<int64_t>(a.W) * swa_row_bytes;
+    }
+    const int n_slots = a.k + a.W;
+
+    const int t_begin = split * a.tiles_per_split;
+    int t_end = t_begin + a.tiles_per_split;
+    if (t_end > a.n_tiles) t_end = a.n_tiles;
+    const int n_it = t_end > t_begin ? t_end - t_begin : 0;
+    const int t_main_end = a.k / KT;        // tiles made only of main-KV slots
+
+    int win0 = t_begin;
+    auto stage_idx = [&](int first_tile) {
+        win0 = first_tile;
+        for (int i = tid; i < kMaxTilesPerSplit * KT; i += 512) {
+            const int slot = first_tile * KT + i;
+            idx_s[i] = slot < a.k ? idx[slot] : -1;
+        }
+    };
+    stage_idx(t_begin);
+
+    // ---- role registers: R holds the q fragments of an S-wave (32 k-steps
+    // x 4 dwords) or the O^T accumulators of a D-wave (4 d tiles x 2 head
+    // tiles); a wave keeps one role for the whole kernel, so the two share
+    // the same 128 registers
+    floatx16 R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) R[i][r] = 0.0f;
+    auto qfrag = [&](int st) {
+        const int b = 4 * (st & 3);
+        return __builtin_bit_cast(half8, make_float4(R[st >> 2][b], R[st >> 2][b + 1], R[st >> 2][b + 2],
+                                                     R[st >> 2][b + 3]));
+    };
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+    if (s_role) {
+        // H is a multiple of 64 at D = 512, so every head of the block exists
+        const int head = hbase + 32 * hg + (lane & 31);
+        const int64_t qrow = (u * a.H + head) * D;
+#pragma unroll
+        for (int st = 0; st < SSTEPS; ++st) {
+            const int d0 = 16 * st + 8 * (lane >> 5);
+            uint32_t wd[4];
+            if (BF16) {
+                const uint4 r = *reinterpret_cast<const uint4*>(a.q + qrow + d0);
+                const uint32_t in[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wd[e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
+            } else {
+                const float* q32 = reinterpret_cast<const float*>(a.q) + qrow + d0;
+                const uint4 r0 = *reinterpret_cast<const uint4*>(q32);
+                const uint4 r1 = *reinterpret_cast<const uint4*>(q32 + 4);
+                wd[0] = pack_h2(__uint_as_float(r0.x), __uint_as_float(r0.y));
+                wd[1] = pack_h2(__uint_as_float(r0.z), __uint_as_float(r0.w));
+                wd[2] = pack_h2(__uint_as_float(r1.x), __uint_as_float(r1.y));
+                wd[3] = pack_h2(__uint_as_float(r1.z), __uint_as_float(r1.w));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[st >> 2][4 * (st & 3) + e] = __uint_as_float(wd[e]);
+        }
+    }
+
+    // ---- D-wave state: O^T accumulator (d tile mt, head tile nt) is
+    // R[2mt + nt]; the gathered rows of the next main tile (keys 16dw + i,
+    // channels 8lane..) wait in pm_*
+    uint32_t pm_cw[16], pm_sc[16];
+    uint32_t pm_ok = 0;
+    auto prefetch_main = [&](int tile) {
+        pm_ok = 0;
+        // lane i < 16 fetches the index of key 16dw + i; each key's row then
+        // comes out of that lane as a scalar
+        const int32_t rows16 = idx_s[tile * KT + 16 * dw + (lane & 15) - win0 * KT];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int32_t row = __builtin_amdgcn_readlane(rows16, i);
+            const bool ok = row >= 0 && row < a.cap;
+            const int64_t rr = kvbase + (ok ? row : 0);
+            pm_ok |= ok ? (1u << i) : 0u;
+            pm_cw[i] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * lane);
+            pm_sc[i] = a.scales[rr * (D / 16) + (lane >> 1)];
+        }
+    };
+    auto store_key = [&](int buf, int key, const uint32_t (&h)[4], bool valid) {
+        *reinterpret_cast<uint4*>(&Kt[buf][key * KROW + 8 * lane]) = make_uint4(h[0], h[1], h[2], h[3]);
+        if (lane == 0) kmask[buf][key] = valid ? 0.0f : -__builtin_inff();
+    };
+    auto dequant_prefetched = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t h[4];
+            dequant8_hw(pm_cw[i], pm_sc[i], h);
+            // an empty slot keeps the finite values of the clamped row; its
+            // logit is -inf, so it enters P.V with weight exactly 0
+            store_key(buf, 16 * dw + i, h, (pm_ok >> i) & 1u);
+        }
+    };
+    // any tile (main rows, window rows, empty slots), loaded and stored at once
+    auto load_generic = [&](int tile, int buf) {
+        for (int i = 0; i < 16; ++i) {
+            const int key = 16 * dw + i;
+            const int slot = tile * KT + key;
+            uint32_t h[4] = {0u, 0u, 0u, 0u};
+            bool valid = false;
+            if (slot < a.k) {
+                const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * KT]);
+                valid = row >= 0 && row < a.cap;
+                const int64_t rr = kvbase + (valid ? row : 0);
+                const uint32_t cw = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * lane);
+                const uint32_t sc = a.scales[rr * (D / 16) + (lane >> 1)];
+                dequant8_hw(cw, sc, h);
+            } else if (slot < n_slots && slot - a.k < n_swa) {
+                valid = true;
+                const uint8_t* rp = swa_rows + static_cast<int64_t>(slot - a.k) * swa_row_bytes;
+                if (BF16) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(rp + 16 * lane);
+                    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
+                } else {
+                    const uint4 v0 = *reinterpret_cast<const uint4*>(rp + 32 * lane);
+                    const uint4 v1 = *reinterpret_cast<const uint4*>(rp + 32 * lane + 16);
+                    h[0] = pack_h2(__uint_as_float(v0.x), __uint_as_float(v0.y));
+                    h[1] = pack_h2(__uint_as_float(v0.z), __uint_as_float(v0.w));
+                    h[2] = pack_h2(__uint_as_float(v1.x), __uint_as_float(v1.y));
+                    h[3] = pack_h2(__uint_as_float(v1.z), __uint_as_float(v1.w));
+                }
+            }
+            store_key(buf, key, h, valid);
+        }
+    };
+    // O^T += V^T P^T for the tile in Kt[buf] with the P fragments in Pb
+    auto pv_tile = [&](int buf) {
+        if (grow_s[0] | grow_s[1]) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const float al = grow_s[nt] ? alpha_s[32 * nt + (lane & 31)] : 1.0f;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) R[2 * mt + nt][r] *= al;
+            }
+        }
+        const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8 pf0 = __builtin_bit_cast(half8, Pb[0][ks][lane]);
+            const half8 pf1 = __builtin_bit_cast(half8, Pb[1][ks][lane]);
+            // A = V^T[32 d][16 k-slots]: k-slot 8h + i holds key
+            // 16ks + 4h + (i % 4) + 8(i / 4), h = lane / 32 (the P order); the
+            // transposed read hands lane 16g + i' the element i' % 4 of lanes
+            // 4e + i'/4 of its 16-lane group, so lane 16g + jj reads 4
+            // channels of key 16ks + 4(g/2) + jj/4, and 8 keys further on.
+            const int key = 16 * ks + 4 * (g >> 1) + (jj >> 2);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int d = 128 * dw + 32 * mt + 16 * (g & 1) + 4 * (jj & 3);
+                const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4v __attribute__((address_space(3)))*)(&Kt[buf][key * KROW + d]));
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4v __attribute__((address_space(3)))*)(&Kt[buf][(key + 8) * KROW + d]));
+                const short8v vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                const half8 vf = __builtin_bit_cast(half8, vv);
+                R[2 * mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf0, R[2 * mt], 0, 0, 0);
+                R[2 * mt + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf1, R[2 * mt + 1], 0, 0, 0);
+            }
+        }
+    };
+
+    if (tid < 2) grow_s[tid] = 0;
+    __syncthreads();                                  // idx_s staged
+    if (!s_role && n_it > 0) {
+        if (t_begin < t_main_end) {
+            prefetch_main(t_begin);
+            dequant_prefetched(0);
+        } else {
+            load_generic(t_begin, 0);
+        }
+        if (t_begin + 1 < t_end && t_begin + 1 < t_main_end) prefetch_main(t_begin + 1);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_it; ++it) {
+        const int tile = t_begin + it, buf = it & 1;
+        // ---------------- phase 1
+        float t2[16];
+        if (s_role) {
+            // two independent accumulation chains (even / odd k-steps) keep
+            // the matrix core busy across the dependent MFMA latency
+            floatx16 s_acc, s_acc2;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { s_acc[r] = 0.0f; s_acc2[r] = 0.0f; }
+#pragma unroll
+            for (int st = 0; st < SSTEPS; st += 2) {
+                const half8 kf0 = *reinterpret_cast<const half8*>(
+                    &Kt[buf][(32 * kb + (lane & 31)) * KROW + 16 * st + 8 * (lane >> 5)]);
+                const half8 kf1 = *reinterpret_cast<const half8*>(
+                    &Kt[buf][(32 * kb + (lane & 31)) * KROW + 16 * (st + 1) + 8 * (lane >> 5)]);
+                s_acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf0, qfrag(st), s_acc, 0, 0, 0);
+                s_acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf1, qfrag(st + 1), s_acc2, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s_acc[r] += s_acc2[r];
+            const float4* km4 = reinterpret_cast<const float4*>(kmask[buf]);
+            float bmax = -__builtin_inff();
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                // rows 32kb + 8r4 + 4(lane/32) + 0..3
+                const float4 km = km4[8 * kb + 2 * r4 + (lane >> 5)];
+                t2[4 * r4] = fmaf(s_acc[4 * r4], a.c2, km.x);
+                t2[4 * r4 + 1] = fmaf(s_acc[4 * r4 + 1], a.c2, km.y);
+                t2[4 * r4 + 2] = fmaf(s_acc[4 * r4 + 2], a.c2, km.z);
+                t2[4 * r4 + 3] = fmaf(s_acc[4 * r4 + 3], a.c2, km.w);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, t2[r]);
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+            if (lane < 32) Lm[hg][kb][lane] = bmax;
+        } else if (it > 0) {
+            pv_tile(buf ^ 1);
+        }
+        __syncthreads();
+        // ---------------- phase 2
+        if (it + 2 < n_it && tile + 2 - win0 >= kMaxTilesPerSplit) {
+            stage_idx(tile + 1);
+            __syncthreads();
+        }
+        if (s_role) {
+            // tile max over both key blocks (same value in both S-waves of
+            // the head group); the reference moves only when it is exceeded
+            // by more than 8, so p < 2^8 and rescales are rare
+            const float tmax = fmaxf(Lm[hg][0][lane & 31], Lm[hg][1][lane & 31]);
+            const bool grow = tmax > m_run + 8.0f || (m_run == -__builtin_inff() && tmax != -__builtin_inff());
+            const bool any = __ballot(grow) != 0;
+            float al = 1.0f;
+            if (any) {
+                const float m_new = grow ? tmax : m_run;
+                al = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                if (m_new != m_run) l_run *= al;
+                m_run = m_new;
+            }
+            if (kb == 0) {
+                if (lane < 32) alpha_s[32 * hg + lane] = al;
+                if (lane == 0) grow_s[hg] = any ? 1 : 0;
+            }
+            uint32_t pk[8];
+            float psum = 0.0f;
+            if (m_run == -__builtin_inff()) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) pk[q] = 0u;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const half2v ph = {static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[2 * q] - m_run)),
+                                       static_cast<_Float16>(__builtin_amdgcn_exp2f(t2[2 * q + 1] - m_run))};
+                    psum = __builtin_amdgcn_fdot2(ph, half2v{1.0f16, 1.0f16}, psum, false);
+                    pk[q] = __builtin_bit_cast(uint32_t, ph);
+                }
+            }
+            l_run += psum;
+            Pb[hg][2 * kb][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            Pb[hg][2 * kb + 1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        } else if (tile + 1 < t_end) {
+            if (tile + 1 < t_main_end) dequant_prefetched(buf ^ 1);
+            else load_generic(tile + 1, buf ^ 1);
+            if (tile + 2 < t_end && tile + 2 < t_main_end) prefetch_main(tile + 2);
+        }
+        __syncthreads();
+    }
+    if (!s_role && n_it > 0) pv_tile((n_it - 1) & 1);
+
+    // ---------------- epilogue
+    if (s_role) {
+        const float lw = l_run + __shfl_xor(l_run, 32);
+        if (lane < 32) {
+            Lsum[hg][kb][lane] = lw;
+            if (kb == 0) Mfin[32 * hg + lane] = m_run;
+        }
+    }
+    __syncthreads();
+    if (s_role) return;
+    float l_tot[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) l_tot[nt] = Lsum[nt][0][lane & 31] + Lsum[nt][1][lane & 31];
+    if (a.splits == 1) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int head = hbase + 32 * nt + (lane & 31);
+            if (head >= a.H) continue;
+            const float inv = l_tot[nt] > 0.0f ? 1.0f / l_tot[nt] : 0.0f;
+            float* orow = a.out + (u * a.H + head) * D;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = 128 * dw + 32 * mt + 8 * r4 + 4 * (lane >> 5);
+                    const floatx16& o = R[2 * mt + nt];
+                    *reinterpret_cast<float4*>(orow + d) =
+                        make_float4(o[4 * r4] * inv, o[4 * r4 + 1] * inv, o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv);
+                }
+        }
+    } else {
+        // partial layout of combine_kernel<512, 4>: block (w' = 2dw + nt, mt)
+        const int64_t pidx = (u * gridDim.z + hb) * a.splits + split;
+        float* po = a.ws_o + pidx * (64 * D);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    po[(((2 * dw + nt) * 4 + mt) * 16 + r) * 64 + lane] = R[2 * mt + nt][r];
+        if (dw == 0 && lane < 32) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                a.ws_m[pidx * 64 + 32 * nt + lane] = Mfin[32 * nt + lane];
+                a.ws_l[pidx * 64 + 32 * nt + lane] = l_tot[nt];
+            }
         }
     }
 }
@@ -599,13 +959,17 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 
 struct SplitPlan { int splits, tiles_per_split, n_tiles; };
 
-SplitPlan plan(int64_t units, int H, int k, int W) {
+// keys per tile of attn_kernel<D, ...> (8 per thread, 8 * waves)
+constexpr int tile_keys(int D) { return D == 512 ? 64 : 32; }
+
+SplitPlan plan(int64_t units, int H, int k, int W, int KT) {
     SplitPlan p;
-    p.n_tiles = (k + W + kKT - 1) / kKT;
+    p.n_tiles = (k + W + KT - 1) / KT;
     const int64_t hblocks = (H + 63) / 64;
     const int64_t base = units * hblocks;
     int64_t want = (512 + base - 1) / base;          // aim for ~512 workgroups
-    int64_t max_splits = (p.n_tiles + 3) / 4;        // keep >= 4 tiles per split
+    const int min_tiles = 128 / KT;                  // keep >= 128 keys per split
+    int64_t max_splits = (p.n_tiles + min_tiles - 1) / min_tiles;
     if (want > max_splits) want = max_splits;
     if (want > kCombineMaxSplits) want = kCombineMaxSplits;
     if (want < 1) want = 1;
@@ -618,7 +982,7 @@ SplitPlan plan(int64_t units, int H, int k, int W) {
 
 template <int D, int NQ, bool BF16>
 hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
-    const SplitPlan sp = plan(L.units, L.H, L.k, L.W);
+    const SplitPlan sp = plan(L.units, L.H, L.k, L.W, tile_keys(D));
     const int hblocks = (L.H + 63) / 64;
     AttnArgs a;
     a.q = static_cast<const uint16_t*>(L.q); a.q_bf16 = L.q_bf16;
@@ -633,7 +997,13 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     a.ws_m = L.ws ? L.ws + nparts * 64 * D : nullptr;
     a.ws_l = L.ws ? a.ws_m + nparts * 64 : nullptr;
     if (L.units == 0) return hipSuccess;
-    attn_kernel<D, NQ, BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 128 * NQ, 0, st>>>(a);
+    // many query units (prefill chunks, large batches): the warp-specialised
+    // kernel keeps the matrix cores busier; few units: the split kernel has
+    // the shorter start-up
+    if (D == 512 && L.units >= 64)
+        attn_ws_kernel<BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 512, 0, st>>>(a);
+    else
+        attn_kernel<D, NQ, BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 128 * NQ, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sp.splits == 1) return e;
     combine_kernel<D, NQ><<<dim3(static_cast<unsigned>(L.units * hblocks), 2 * NQ * (D / NQ / 32)), 1024, 0, st>>>(
@@ -648,7 +1018,7 @@ bool attn_shape_supported(int H, int D) {
 }
 
 size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W) {
-    const SplitPlan sp = plan(units, H, k, W);
+    const SplitPlan sp = plan(units, H, k, W, tile_keys(D));
     if (sp.splits == 1) return 0;
     const int64_t hblocks = (H + 63) / 64;
     const int64_t nparts = units * hblocks * sp.splits;
