@@ -116,29 +116,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         // Stream the row chunks in groups of G (registers hold the current
         // group and the next one in flight); the group loop is not unrolled
         // so the compiler cannot hoist every load and query read at once.
+        // Every load is unconditional: invisible positions read row 0 of the
+        // sequence and are masked when the score is written, and the last
+        // group's "next" load repeats the last group, so no load sits in a
+        // lane-divergent branch.
+        constexpr int NG = NCH / G;
         uint4 cur[2][G];
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-                cur[p][j] = pos[p] >= 0 ? *reinterpret_cast<const uint4*>(base[p] + j * 1024)
-                                        : make_uint4(0, 0, 0, 0);
+            for (int p = 0; p < 2; ++p) cur[p][j] = *reinterpret_cast<const uint4*>(base[p] + j * 1024);
         float acc[2][HI];
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
             for (int h = 0; h < HI; ++h) acc[p][h] = 0.0f;
 #pragma unroll 1
-        for (int g = 0; g < NCH / G; ++g) {
+        for (int g = 0; g < NG; ++g) {
+            const int gn = g + 1 < NG ? g + 1 : g;
             uint4 nxt[2][G];
-            const bool more = g + 1 < NCH / G;
 #pragma unroll
             for (int j = 0; j < G; ++j)
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
-                    nxt[p][j] = (more && pos[p] >= 0)
-                                    ? *reinterpret_cast<const uint4*>(base[p] + ((g + 1) * G + j) * 1024)
-                                    : make_uint4(0, 0, 0, 0);
+                    nxt[p][j] = *reinterpret_cast<const uint4*>(base[p] + (gn * G + j) * 1024);
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const int c = g * G + j;
