@@ -328,6 +328,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=ci.DECODE_128K.name, choices=sorted(ci.WORKLOADS))
     ap.add_argument("--cpu-queries", type=int, default=8, help="oracle sample size (0 = skip)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the prefill chunk workload (profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
@@ -347,6 +349,9 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, 4, dev)
+        return 0
+    if args.prefill_only:
+        print(json.dumps(run_prefill(K, ci.PREFILL_CHUNK, args.steps, args.warmup, dev)), flush=True)
         return 0
     w = ci.WORKLOADS[args.workload]
     if "F" not in w.schedule:
