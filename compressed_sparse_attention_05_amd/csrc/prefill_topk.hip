@@ -4,35 +4,50 @@
 //
 // The indices must equal those chosen from the exact score (float32 fma
 // chains over channels, then over heads, in order).  That order cannot be
-// kept on the matrix cores, so the selection runs in two tiers:
+// kept on the matrix cores, so the selection runs in tiers:
 //
-//  1. score_mfma_kernel computes s~ = sum_h w_h ReLU(q_h . k_j) for a block of
-//     queries x keys with v_mfma_f32_32x32x16_bf16 (bf16 products are exact
-//     in float32; only the order and precision of the additions differ);
-//  2. for each query row, |s~_j - s_j| <= eps_t for every key j, where
-//         eps_t = kEpsRel * A_t * Kmax + (underflow term),
-//         A_t   = sum_h |w_h| * ||q_h||_2,   Kmax = max_j ||k_j||_2.
-//     Derivation: each dot product of n = 128 exact products summed in
-//     float32 in any order, each addition rounded at least as well as
-//     truncation (unit 2^-23), is within gamma_n * sum_c |q_c k_c| of the
-//     real value (gamma_n = n 2^-23 / (1 - n 2^-23) = 1.53e-5), so the exact
-//     chain and the matrix-core sum differ by at most 2 gamma_n ||q_h|| ||k_j||
-//     (Cauchy-Schwarz); ReLU is 1-Lipschitz; the two 8-term head sums add
-//     at most 2 gamma_8 (2^-24 unit) of sum_h |w_h| ||q_h|| ||k_j|| (1 + ...).
-//     Total below 3.2e-5 * A_t * ||k_j||; kEpsRel = 4e-5 leaves margin for
-//     the float32 norms themselves.
-//     With tau~ the k-th largest s~ (the exact k-th score tau is within eps of
-//     it): s~ > tau~ + 2 eps  =>  s > tau (chosen);  s~ < tau~ - 2 eps  =>
-//     s < tau (not chosen); keys in between are rescored with the exact
-//     chain, and the remaining slots go to them by (exact score desc,
+//  1. Bound.  The matrix cores give s~ = sum_h w_h ReLU(q_h . k_j) with
+//     v_mfma_f32_32x32x16_bf16 (bf16 products are exact in float32; only the
+//     order and precision of the additions differ), and for every key j
+//         |s~_j - s_j| <= eps_t = kEpsRel * A_t * Kmax + (underflow term),
+//         A_t = sum_h |w_h| * ||q_h||_2,   Kmax = max_j ||k_j||_2.
+//     Derivation: a dot product of n = 128 exact products summed in float32
+//     in any order, each addition rounded at least as well as truncation
+//     (unit 2^-23), is within gamma_n * sum_c |q_c k_c| of the real value
+//     (gamma_n = n 2^-23 / (1 - n 2^-23) = 1.53e-5), so the exact chain and
+//     the matrix-core sum differ by at most 2 gamma_n ||q_h|| ||k_j||
+//     (Cauchy-Schwarz); ReLU is 1-Lipschitz; the two 8-term head sums add at
+//     most 2 gamma_8 of sum_h |w_h| ||q_h|| ||k_j|| (1 + ...).  Total below
+//     3.2e-5 * A_t * ||k_j||; kEpsRel = 4e-5 leaves margin for the float32
+//     norms themselves.
+//  2. Sample.  s~ of one 32-key block in every 512 keys (the block picked by
+//     a hash of the group, so periodic structure cannot alias) gives each row a
+//     lower key L_t: the sample's j-th largest, j chosen so that about 3k
+//     keys of the whole row are expected at or above it.
+//  3. Candidates.  The full matrix-core pass keeps (s~, position) of every
+//     key with s~ >= L_t; each workgroup owns a fixed slot range per row
+//     (as many slots as it has keys), so no atomics are needed.
+//  4. Final, per row: with C candidates, k <= C and tau~ the k-th largest
+//     candidate s~ (then also the k-th of the whole row, since every other
+//     key lies below L_t), the check L_t <= tau~ - 2 eps shows that every key
+//     within 2 eps of tau~ or above is a candidate.  Then s~ > tau~ + 2 eps
+//     => s > tau (chosen), s~ < tau~ - 2 eps => s < tau (not chosen), where
+//     tau is the exact k-th score; keys in between are rescored with the
+//     exact chain and fill the remaining slots by (exact score desc,
 //     position asc).  Every key whose exact score equals tau lies in that
 //     band, so ties resolve exactly as in the definition.
 //
-// Rows whose candidate list or band does not fit the fixed LDS budget fall
-// back to exact scores for the whole row (same result, slower).
+// A row that fails a check (too few or too many candidates, a band wider
+// than the fixed LDS budget) is rescored exactly over its whole row and
+// selected with the same radix routine as csa2_topk: same result, slower.
 //
-// Scratch (per chunk of up to kChunkRows query rows): the s~ rows, a 4,096-bin
-// histogram per row, and the candidate list per row.
+// Scratch per chunk of up to kChunkRows query rows: the sample's s~, and the
+// candidate slots (8 bytes per (row, visible key) reserved, a few percent
+// written), which a falling-back row reuses for its exact scores.
+//
+// Launch shape: the scoring grids are sized to whole rounds of one
+// workgroup per CU, and numbered so the workgroups that read the same keys
+// share an XCD's L2.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -44,14 +59,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHeads = 8, kDim = 128;          // indexer shape of the matrix-core path
 constexpr int kNch = kDim * 2 / 16;            // 16-byte chunks per indexer row
-constexpr int kBins = 4096;                    // coarse digit: key >> 20
-constexpr int kCandCap = 12288;                // candidates per row kept for the final pass
+constexpr int kCandCap = 12288;                // candidates per row staged in LDS
 constexpr int kBandCap = 2048;                 // band keys rescored in LDS
 constexpr int kKCap = 4096;                    // largest k
 constexpr int kChunkRows = 1024;               // query rows per scratch chunk
 constexpr int kQB = 64;                        // queries per scoring workgroup
-constexpr int kKeyTile = 32;
-constexpr int kKeysPerWG = 4096;
+constexpr int kSub = 32;                       // keys per MFMA column block
+constexpr int kTileKeys = 128;                 // keys per LDS tile (4 column blocks)
+constexpr int kMaxKeysPerWG = 8192;            // largest key range of a candidate workgroup
+constexpr int kGroup = 512;                    // sample: one 32-key block per 512 keys
 constexpr float kEpsRel = 4.0e-5f;
 
 struct PfArgs {
@@ -149,23 +165,89 @@ __global__ __launch_bounds__(256) void eps_kernel(PfArgs a, const uint32_t* __re
     }
 }
 
-// ---------------------------------------------------------------- s~ rows
-// Block = 8 waves x 8 queries (two 32-row M-tiles of 4 queries x 8 heads
-// each) x kKeysPerWG keys, streamed in tiles of 32 keys through LDS
-// (double-buffered).  A = q rows (registers), B = key rows (LDS).
-// Output: st[(t - t0) * ld + j] for t in the chunk, j < n_cols; -inf where
-// j >= vis(t).
-__global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, int64_t t1, int64_t n_cols,
-                                                         int64_t ld, float* __restrict__ st) {
+// ---------------------------------------------------------------- s~ blocks
+// One workgroup = 8 waves x 8 queries (two 32-row M-tiles of 4 queries x 8
+// heads each); A = q rows (registers), B = key rows from LDS.  Keys stream
+// through LDS in tiles of 128 (double-buffered; the next tile's global loads
+// are issued before the current tile's 64 MFMAs per wave).  Each 32-key
+// column block ends in the epilogue: ReLU and head weights give per-lane
+// partial sums over 4 heads, and one v_permlane32_swap pairs the halves, so
+// lane l ends with s~ of key l%32 for query e (l < 32) or 2 + e (l >= 32) of
+// M-tile mt, for e = 0, 1.
+//
+// Workgroup (bx, by) takes query block by and column blocks
+// [bx * g.blocks, (bx + 1) * g.blocks).  The grid is 1-D and, with g.xcd,
+// numbered so that the workgroups of one bx (which read the same keys) run on
+// one XCD and share its L2: dispatch assigns workgroup L to XCD L % 8.
+// SAMPLE: column block b is the hashed 32-key block of group b (kGroup keys
+// per group); s~ goes to samp[row][32 * group + l%32] (-inf where invisible).
+// Otherwise: column block b holds keys [32b, 32b + 32); the workgroup appends
+// (s~ bits, position) for s~ >= L_row to the row's slots [bx * kpw, ...),
+// kpw = 32 * g.blocks, in position order, and its count to counts[row][bx].
+struct Geo {
+    int64_t n_x;         // workgroups per query block that hold keys
+    int32_t n_y;         // query blocks
+    int32_t blocks;      // 32-key column blocks per workgroup (a multiple of 4)
+    int32_t xcd;         // XCD-aware numbering (grid = roundup(n_x, 8) * n_y)
+    int64_t cand_ld;     // candidate slots per row
+    int64_t cnt_ld;      // count entries per row
+};
+__device__ __forceinline__ int sample_block(int64_t group) {
+    return static_cast<int>((static_cast<uint32_t>(group) * 0x9E3779B1u) >> 29) & (kGroup / kSub - 1);
+}
+
+// float threshold of a row's candidate key: 1 -> -inf (every visible key),
+// 0xffffffff -> +inf (none), else the float whose key it is
+__device__ __forceinline__ float thr_float(uint32_t key) {
+    if (key <= 1u) return -__builtin_inff();
+    if (key == 0xffffffffu) return __builtin_inff();
+    return float_of_key(key);
+}
+
+// ReLU as one integer max: non-negative floats order like their bit
+// patterns, and every negative float (and -0) maps to +0
+__device__ __forceinline__ float relu(float x) {
+    const int i = __float_as_int(x);
+    return __int_as_float(i > 0 ? i : 0);
+}
+
+constexpr int kStage = kTileKeys;              // staged candidates per query row per tile (<= its keys)
+
+template <bool SAMPLE>
+__global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, int64_t t1, int64_t n_cols, Geo g,
+                                                         float* __restrict__ samp, int64_t ld_s,
+                                                         const uint32_t* __restrict__ thr,
+                                                         uint32_t* __restrict__ counts, uint2* __restrict__ cand) {
     constexpr int KROW = kDim + 8;               // padded LDS row (bf16 elements)
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeyTile * KROW];
+    constexpr int kStageWords = SAMPLE ? 1 : 8 * (8 * kStage + 64);   // per wave: 8 rows + one dummy slot per lane
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTileKeys * KROW];
+    __shared__ __attribute__((aligned(16))) uint2 stage_all[SAMPLE ? 1 : kStageWords];
+    int64_t bx;
+    int by;
+    {
+        const int64_t L = blockIdx.x;
+        if (g.xcd) {
+            const int64_t i = L >> 3;
+            bx = (L & 7) + 8 * (i / g.n_y);
+            by = static_cast<int>(i % g.n_y);
+        } else {
+            bx = L % g.n_x;
+            by = static_cast<int>(L / g.n_x);
+        }
+    }
+    if (bx >= g.n_x) return;                     // padding of the XCD-aware grid
+    const int n_tiles = g.blocks / (kTileKeys / kSub);
     const int tid = threadIdx.x, lane = tid & 63;
+    const bool hi = lane >= 32;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t qb = t0 + static_cast<int64_t>(blockIdx.y) * kQB + 8 * wv;   // wave's first query
-    const int64_t j_begin = static_cast<int64_t>(blockIdx.x) * kKeysPerWG;
-    int64_t j_end = j_begin + kKeysPerWG;
-    if (j_end > n_cols) j_end = n_cols;
-    const int n_tiles = static_cast<int>((j_end - j_begin + kKeyTile - 1) / kKeyTile);
+    const int64_t qb = t0 + static_cast<int64_t>(by) * kQB + 8 * wv;   // wave's first query
+
+    // first key of column block b of this workgroup
+    auto block_key = [&](int b) -> int64_t {
+        const int64_t gb = bx * g.blocks + b;
+        if (SAMPLE) return gb * kGroup + kSub * sample_block(gb);
+        return gb * kSub;
+    };
 
     // q fragments: M-tile mt, row r = lane%32 -> query qb + 4mt + r/8, head r%8;
     // k-step s covers channels 16s + 8(lane/32) + 0..7
@@ -181,177 +263,198 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     }
     // head weights of the accumulator rows: reg r -> query r/4, head 4(lane/32) + r%4
     float wr[2][16];
-    int64_t vis[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             int64_t t = qb + 4 * mt + qq;
-            vis[mt][qq] = t < t1 ? vis_of(a, t) : 0;
             if (t >= t1) t = t1 - 1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) wr[mt][4 * qq + i] = a.w[t * kHeads + 4 * (lane >> 5) + i];
         }
-    }
+    // per lane and (mt, e): its query's visible limit minus lane%32 (key
+    // block jb is visible for this lane while jb < lim), threshold, and the
+    // staging slots of its row (row index 4mt + query within the M-tile)
+    int32_t lim[2][2];
+    float thf[2][2];
+    float* sbase[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int64_t t = qb + 4 * mt + (hi ? 2 + e : e);
+            const bool ok = t < t1;
+            const int64_t tc = ok ? t : t1 - 1;
+            int64_t v = ok ? vis_of(a, t) : 0;
+            if (v > n_cols) v = n_cols;
+            lim[mt][e] = static_cast<int32_t>(v - (lane & 31));
+            thf[mt][e] = SAMPLE ? 0.0f : thr_float(thr[tc - t0]);
+            sbase[mt][e] = SAMPLE ? samp + (tc - t0) * ld_s + (lane & 31) : nullptr;
+        }
+    uint2* stage = stage_all + (SAMPLE ? 0 : wv * (8 * kStage + 64));
+    // uniform counters per wave row (4mt + query): staged this tile, emitted so far
+    uint32_t c_tile[8], c_glob[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) { c_tile[q] = 0; c_glob[q] = 0; }
 
-    // key tile loader: thread -> (chunk c = tid / 32, key tid % 32)
+    // tile loader: thread -> chunk c = tid / 32 of key (tid % 32) in each of
+    // the tile's 4 column blocks.  Consecutive candidate tiles are 128 keys
+    // (two 64-key cache tiles, 32 KiB) apart, so the addresses advance by a
+    // constant; a tile reaching past the cache clamps per key.
     const int lc = tid >> 5, lk = tid & 31;
-    auto load_tile = [&](int tile) -> uint4 {
-        const int64_t pos = j_begin + static_cast<int64_t>(tile) * kKeyTile + lk;
-        const int64_t p = pos < a.cap ? pos : 0;
-        return *kchunk(a.kc, p, lc);
+    uint4 n0, n1, n2, n3;
+    auto load_tile = [&](int tile) {
+        const int64_t kb0 = block_key(4 * tile);
+        if (!SAMPLE && kb0 + kTileKeys <= a.cap) {
+            const uint4* p = kchunk(a.kc, kb0 + lk, lc);        // +32 keys = +32 entries; +64 keys = next cache tile
+            n0 = p[0]; n1 = p[32]; n2 = p[kNch * 64]; n3 = p[kNch * 64 + 32];
+        } else {
+            int64_t p0 = block_key(4 * tile + 0) + lk, p1 = block_key(4 * tile + 1) + lk;
+            int64_t p2 = block_key(4 * tile + 2) + lk, p3 = block_key(4 * tile + 3) + lk;
+            n0 = *kchunk(a.kc, p0 < a.cap ? p0 : 0, lc);
+            n1 = *kchunk(a.kc, p1 < a.cap ? p1 : 0, lc);
+            n2 = *kchunk(a.kc, p2 < a.cap ? p2 : 0, lc);
+            n3 = *kchunk(a.kc, p3 < a.cap ? p3 : 0, lc);
+        }
     };
-    auto store_tile = [&](int buf, uint4 v) {
-        *reinterpret_cast<uint4*>(&Ks[buf][lk * KROW + 8 * lc]) = v;
+    auto store_tile = [&](int buf) {
+        uint16_t* d = &Ks[buf][lk * KROW + 8 * lc];
+        *reinterpret_cast<uint4*>(d) = n0;
+        *reinterpret_cast<uint4*>(d + kSub * KROW) = n1;
+        *reinterpret_cast<uint4*>(d + 2 * kSub * KROW) = n2;
+        *reinterpret_cast<uint4*>(d + 3 * kSub * KROW) = n3;
     };
-    if (n_tiles > 0) store_tile(0, load_tile(0));
+    load_tile(0);
+    store_tile(0);
     __syncthreads();
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int buf = tile & 1;
-        uint4 nxt = make_uint4(0u, 0u, 0u, 0u);
-        if (tile + 1 < n_tiles) nxt = load_tile(tile + 1);
-        floatx16 acc[2];
+        if (tile + 1 < n_tiles) load_tile(tile + 1);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int i = 0; i < 4; ++i) {
+            // every block is computed (loads of keys past the end read row 0);
+            // invisible keys are masked below
+            const int64_t jb = block_key(4 * tile + i);
+            floatx16 acc[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const bf16x8 kb = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(lane & 31) * KROW + 16 * s + 8 * (lane >> 5)]));
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb, acc[1], 0, 0, 0);
-        }
-        // epilogue: ReLU, head weights, the two 4-head halves joined across
-        // lanes l and l^32
-        const int64_t j = j_begin + static_cast<int64_t>(tile) * kKeyTile + (lane & 31);
+                for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            float part[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                float p = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p = fmaf(wr[mt][4 * qq + i], fmaxf(acc[mt][4 * qq + i], 0.0f), p);
-                part[qq] = p;
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 kb = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(kSub * i + (lane & 31)) * KROW + 16 * s +
+                                                                     8 * (lane >> 5)]));
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb, acc[1], 0, 0, 0);
             }
-            float full[4];
+            const int32_t jb32 = static_cast<int32_t>(jb < 0x7fffffff ? jb : 0x7fffffff);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) full[qq] = part[qq] + __shfl_xor(part[qq], 32);
-            // lanes < 32 write queries 0,1 of the tile, lanes >= 32 queries 2,3
+            for (int mt = 0; mt < 2; ++mt) {
+                float part[4];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int qq = 2 * (lane >> 5) + e;
-                const int64_t t = qb + 4 * mt + qq;
-                if (t < t1 && j < j_end) {
-                    const float v = (qq == 0 ? full[0] : qq == 1 ? full[1] : qq == 2 ? full[2] : full[3]);
-                    const int64_t vq = (qq == 0 ? vis[mt][0] : qq == 1 ? vis[mt][1] : qq == 2 ? vis[mt][2] : vis[mt][3]);
-                    st[(t - t0) * ld + j] = j < vq ? v : -__builtin_inff();
+                for (int qq = 0; qq < 4; ++qq) {
+                    float p = wr[mt][4 * qq] * relu(acc[mt][4 * qq]);
+#pragma unroll
+                    for (int h = 1; h < 4; ++h) p = fmaf(wr[mt][4 * qq + h], relu(acc[mt][4 * qq + h]), p);
+                    part[qq] = p;
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[e]),
+                                                                     __float_as_uint(part[2 + e]), false, false);
+                    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                    const bool vis_ok = jb32 < lim[mt][e];
+                    if (SAMPLE) {
+                        const int64_t gi = jb / kGroup;
+                        if (gi * kSub < ld_s) sbase[mt][e][gi * kSub] = vis_ok ? v : -__builtin_inff();
+                    } else {
+                        // stage (s~ bits, position) of taken keys in row order;
+                        // lanes that take nothing write their dummy slot
+                        const bool take = vis_ok && v >= thf[mt][e];
+                        const uint64_t bal = __ballot(take);
+                        const uint32_t blo = static_cast<uint32_t>(bal), bhi = static_cast<uint32_t>(bal >> 32);
+                        const uint32_t n_lo = static_cast<uint32_t>(__builtin_popcount(blo));
+                        const uint32_t n_hi = static_cast<uint32_t>(__builtin_popcount(bhi));
+                        const int qlo = 4 * mt + e, qhi = 4 * mt + 2 + e;
+                        const uint32_t base = hi ? qhi * kStage + c_tile[qhi] - n_lo : qlo * kStage + c_tile[qlo];
+                        const uint32_t at = __builtin_amdgcn_mbcnt_hi(bhi, __builtin_amdgcn_mbcnt_lo(blo, base));
+                        const uint32_t slot = take ? at : 8 * kStage + lane;
+                        stage[slot] = make_uint2(__float_as_uint(v), static_cast<uint32_t>(jb32) + (lane & 31));
+                        c_tile[qlo] += n_lo;
+                        c_tile[qhi] += n_hi;
+                    }
                 }
             }
         }
-        if (tile + 1 < n_tiles) store_tile(buf ^ 1, nxt);
+        if (!SAMPLE) {
+            // flush the staged candidates of the wave's 8 rows to their slot ranges
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t t = qb + q;
+                if (c_tile[q] > 0u && t < t1) {
+                    uint2* dst = cand + (t - t0) * g.cand_ld + bx * (kSub * g.blocks) + c_glob[q];
+                    for (uint32_t x = lane; x < c_tile[q]; x += 64) dst[x] = stage[q * kStage + x];
+                }
+                c_glob[q] += c_tile[q];
+                c_tile[q] = 0;
+            }
+        }
+        if (tile + 1 < n_tiles) store_tile(buf ^ 1);
         __syncthreads();
     }
+    if (!SAMPLE && lane < 8) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) c = lane == q ? c_glob[q] : c;
+        const int64_t t = qb + lane;
+        if (t < t1) counts[(t - t0) * g.cnt_ld + bx] = c;
+    }
 }
 
-// ---------------------------------------------------------------- selection
-// Per-row candidate threshold: the 4,096-bin histogram gives the bin b* that
-// holds the k-th s~; candidates are keys >= key_of(L), L = lower edge of b*
-// minus 2 eps (rounded down), so every key within 2 eps of tau~ or above is
-// one.  One 256-thread workgroup per row; thread t owns bins 4095-16t down
-// to 4080-16t.
-__global__ __launch_bounds__(256) void band_thresh_kernel(int64_t t0, PfArgs a, const float* __restrict__ eps,
-                                                          const uint32_t* __restrict__ hist_all,
-                                                          uint32_t* __restrict__ thr) {
-    __shared__ uint32_t wsum[4];
+// ---------------------------------------------------------------- threshold
+// L_t per row: rows with vis <= k need no candidates (all chosen); rows with
+// vis <= kCandCap take every visible key; otherwise L_t is the j-th largest
+// sampled s~, j = round(target * n_s / vis) with n_s visible sampled keys and
+// about target = min(3k, (k + kCandCap) / 2) keys expected at or above it.
+// The sample row is staged in LDS when it fits.
+constexpr int kSampLds = 16384;
+__global__ __launch_bounds__(kThreads) void sample_thresh_kernel(int64_t t0, PfArgs a, const float* __restrict__ samp,
+                                                                 int64_t ld_s, uint32_t* __restrict__ thr) {
+    __shared__ uint32_t sk[kSampLds];
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wave_tot[kWaves];
+    __shared__ uint32_t res[2];
     const int64_t r = blockIdx.x;
-    const int64_t t = t0 + r;
-    const int64_t vis = vis_of(a, t);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (vis <= a.k) {                                  // whole row chosen
-        if (tid == 0) thr[r] = 1u;
+    const int64_t vis = vis_of(a, t0 + r);
+    if (vis <= a.k) {
+        if (threadIdx.x == 0) thr[r] = 0xffffffffu;
         return;
     }
-    const uint32_t need = static_cast<uint32_t>(a.k);
-    const int hb = kBins - 16 - 16 * tid;
-    uint32_t c[16], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&hist_all[r * kBins + hb + i]);
-        c[15 - i] = v.x; c[14 - i] = v.y; c[13 - i] = v.z; c[12 - i] = v.w;
+    if (vis <= kCandCap) {
+        if (threadIdx.x == 0) thr[r] = 1u;
+        return;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sum += c[i];                 // c[0] is the highest bin
-    uint32_t incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wv; ++w) before += wsum[w];
-    const uint32_t excl = before + incl - sum;
-    if (excl < need && excl + sum >= need) {
-        uint32_t acc = excl;
-        int bin = hb;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (acc + c[i] >= need) { bin = hb + 15 - i; break; }
-            acc += c[i];
-        }
-        const float L = next_down(float_of_key(static_cast<uint32_t>(bin) << 20) - 2.0f * eps[t]);
-        const uint32_t lk = key_of(L);
-        thr[r] = lk > 0u ? lk : 1u;
-    }
-}
-
-// Append (key, position) of every candidate (key >= thr[row]) to the row's
-// list; one global atomic per wave.
-__global__ __launch_bounds__(kThreads) void band_collect_kernel(const float* __restrict__ st, int64_t ld,
-                                                                int64_t t0, PfArgs a,
-                                                                const uint32_t* __restrict__ thr,
-                                                                uint32_t* __restrict__ cnt,
-                                                                uint2* __restrict__ cand) {
-    constexpr int kPer = 16;
-    constexpr int kChunk = kPer * kThreads;
-    const int64_t r = blockIdx.y;
-    const int64_t vis = vis_of(a, t0 + r);
-    if (vis <= a.k) return;                           // whole row chosen: no candidates needed
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk;
-    if (base >= vis) return;
-    const float* s = st + r * ld;
-    const uint32_t lkey = thr[r];
-    const int lane = threadIdx.x & 63;
-    uint32_t kk[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int64_t i = base + j * kThreads + threadIdx.x;
-        kk[j] = (i < vis) ? key_of(s[i]) : 0u;
-    }
-    uint64_t bal[kPer];
-    uint32_t tot = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        bal[j] = __ballot(kk[j] >= lkey);
-        tot += static_cast<uint32_t>(__popcll(bal[j]));
-    }
-    if (tot == 0) return;
-    uint32_t wb = 0;
-    if (lane == 0) wb = atomicAdd(&cnt[r], tot);
-    wb = __shfl(wb, 0);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const uint32_t off = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[j] >> 32),
-                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[j]), 0u));
-        const uint32_t at = wb + off;
-        if (((bal[j] >> lane) & 1ull) && at < static_cast<uint32_t>(kCandCap)) {
-            const int64_t i = base + j * kThreads + threadIdx.x;
-            cand[r * kCandCap + at] = make_uint2(kk[j], static_cast<uint32_t>(i));
-        }
-        wb += static_cast<uint32_t>(__popcll(bal[j]));
+    int64_t n = (vis + kGroup - 1) / kGroup * kSub;
+    if (n > ld_s) n = ld_s;
+    const float* s = samp + r * ld_s;
+    const double target = fmin(3.0 * a.k, 0.5 * (a.k + kCandCap));
+    auto pick = [&](auto get) {
+        const uint32_t n_s = count_valid(get, n, wave_tot);
+        const double jd = target * static_cast<double>(n_s) / static_cast<double>(vis) + 0.5;
+        uint32_t j = static_cast<uint32_t>(jd);
+        if (j < 1u) j = 1u;
+        if (j > n_s) j = n_s;
+        uint32_t T = 1u, need = 0;
+        if (n_s > 0) radix_select(get, n, j, hist, res, T, need);
+        if (threadIdx.x == 0) thr[r] = T > 0u ? T : 1u;
+    };
+    if (n <= kSampLds) {
+        for (int64_t i = threadIdx.x; i < n; i += kThreads) sk[i] = key_of(s[i]);
+        __syncthreads();
+        pick([&](int64_t i) { return sk[i]; });
+    } else {
+        pick([&](int64_t i) { return key_of(s[i]); });
     }
 }
 
@@ -380,10 +483,11 @@ __device__ float exact_score(const float* qf, const float* wf, const uint8_t* kc
     return s;
 }
 
-__global__ __launch_bounds__(kThreads) void band_final_kernel(float* __restrict__ st, int64_t ld, int64_t t0,
-                                                              PfArgs a, const float* __restrict__ eps,
-                                                              const uint32_t* __restrict__ cnt,
-                                                              const uint2* __restrict__ cand_all,
+__global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs a, const float* __restrict__ eps,
+                                                              const uint32_t* __restrict__ thr,
+                                                              const uint32_t* __restrict__ counts, int64_t cnt_ld,
+                                                              int64_t cand_ld, int64_t kpw,
+                                                              uint2* __restrict__ cand_all,
                                                               int32_t* __restrict__ out) {
     __shared__ uint2 cand[kCandCap];
     __shared__ uint64_t band[kBandCap];
@@ -398,88 +502,140 @@ __global__ __launch_bounds__(kThreads) void band_final_kernel(float* __restrict_
     const int64_t t = t0 + r;
     const int64_t vis = vis_of(a, t);
     const int k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int32_t* o = out + t * static_cast<int64_t>(k);
     const uint32_t k_eff = vis < k ? static_cast<uint32_t>(vis) : static_cast<uint32_t>(k);
     if (vis <= k) {                                   // every visible entry is chosen
-        for (int64_t i = threadIdx.x; i < k; i += kThreads) o[i] = i < vis ? static_cast<int32_t>(i) : -1;
+        for (int64_t i = tid; i < k; i += kThreads) o[i] = i < vis ? static_cast<int32_t>(i) : -1;
         return;
     }
     // query row in float32 (exact widening of bf16)
-    for (int i = threadIdx.x; i < kHeads * kDim; i += kThreads) {
+    for (int i = tid; i < kHeads * kDim; i += kThreads) {
         const uint16_t b = a.q[t * kHeads * kDim + i];
         qf[i] = __uint_as_float(static_cast<uint32_t>(b) << 16);
     }
-    if (threadIdx.x < kHeads) wf[threadIdx.x] = a.w[t * kHeads + threadIdx.x];
-    const uint32_t C = cnt[r];
-    bool fallback = C > static_cast<uint32_t>(kCandCap);
+    if (tid < kHeads) wf[tid] = a.w[t * kHeads + tid];
+    const uint32_t* crow = counts + r * cnt_ld;
+    uint2* region = cand_all + r * cand_ld;
+    const int64_t n_seg = (vis + kpw - 1) / kpw;   // workgroups that saw visible keys
+
+    // total candidates
+    uint32_t part = 0;
+    for (int64_t sgi = tid; sgi < n_seg; sgi += kThreads) part += crow[sgi];
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) wave_tot[wv] = part;
+    __syncthreads();
+    uint32_t C = 0;
+    for (int i = 0; i < kWaves; ++i) C += wave_tot[i];
+    __syncthreads();
+    const uint32_t L = thr[r];
+    bool fallback = C > static_cast<uint32_t>(kCandCap) || C < k_eff;
     if (!fallback) {
-        for (uint32_t i = threadIdx.x; i < C; i += kThreads) cand[i] = cand_all[r * kCandCap + i];
+        // gather the segments into LDS: hist[0..1023] = segment offsets,
+        // hist[1024..2047] = counts, 1,024 segments at a time
+        uint32_t running = 0;
+        for (int64_t sb = 0; sb < n_seg; sb += kThreads) {
+            const int64_t sgi = sb + tid;
+            const uint32_t c = sgi < n_seg ? crow[sgi] : 0u;
+            uint32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t x = __shfl_up(incl, off);
+                if (lane >= off) incl += x;
+            }
+            if (lane == 63) wave_tot[wv] = incl;
+            __syncthreads();
+            uint32_t before = 0, tot = 0;
+            for (int i = 0; i < kWaves; ++i) {
+                before += i < wv ? wave_tot[i] : 0u;
+                tot += wave_tot[i];
+            }
+            hist[tid] = running + before + incl - c;
+            hist[1024 + tid] = c;
+            __syncthreads();
+            const int n_here = static_cast<int>(n_seg - sb < kThreads ? n_seg - sb : kThreads);
+            for (int s = wv; s < n_here; s += kWaves) {
+                const uint32_t so = hist[s], sc = hist[1024 + s];
+                const uint2* src = region + (sb + s) * kpw;
+                for (uint32_t i = lane; i < sc; i += 64) cand[so + i] = src[i];
+            }
+            running += tot;
+            __syncthreads();
+        }
+        // keys of s~ (candidates hold the float bits), in position order
+        for (uint32_t i = tid; i < C; i += kThreads) cand[i].x = key_of(__uint_as_float(cand[i].x));
         __syncthreads();
-        // tau~: the k-th largest s~ (all keys at or above it are candidates)
+        // tau~: the k-th largest s~ (of the candidates, and of the row)
         uint32_t T = 0, need = 0;
         auto get = [&](int64_t i) { return cand[i].x; };
         radix_select(get, C, k_eff, hist, res, T, need);
         const float tau = float_of_key(T);
         const float e2 = 2.0f * eps[t];
         const uint32_t hi_key = key_of(next_up(tau + e2));
-        const uint32_t lo_key = key_of(next_down(tau - e2)) > 0u ? key_of(next_down(tau - e2)) : 1u;
-        if (threadIdx.x < 2) counters[threadIdx.x] = 0;
+        const uint32_t lo_raw = key_of(next_down(tau - e2));
+        const uint32_t lo_key = lo_raw > 0u ? lo_raw : 1u;
+        if (tid < 2) counters[tid] = 0;
         __syncthreads();
-        // sure picks (s~ above the band) -> sel; band keys -> band
-        for (uint32_t i = threadIdx.x; i < C; i += kThreads) {
-            const uint2 c = cand[i];
-            if (c.x > hi_key) {
-                const uint32_t at = atomicAdd(&counters[0], 1u);
-                if (at < static_cast<uint32_t>(kKCap)) sel[at] = c.y;
-            } else if (c.x >= lo_key) {
-                const uint32_t at = atomicAdd(&counters[1], 1u);
-                if (at < static_cast<uint32_t>(kBandCap)) band[at] = c.y;
-            }
-        }
-        __syncthreads();
-        const uint32_t n_in = counters[0], n_band = counters[1];
-        if (n_band > static_cast<uint32_t>(kBandCap) || n_in > k_eff || n_in + n_band < k_eff) {
-            fallback = true;
+        if (lo_key < L) {
+            fallback = true;                          // the band reaches below L_t
         } else {
-            // exact scores of the band keys; order by (score desc, position
-            // asc) via an ascending sort of (~key << 32 | position)
-            for (uint32_t i = threadIdx.x; i < n_band; i += kThreads) {
-                const uint32_t pos = static_cast<uint32_t>(band[i]);
-                const uint32_t ek = key_of(exact_score(qf, wf, a.kc, pos));
-                band[i] = (static_cast<uint64_t>(~ek) << 32) | pos;
-            }
-            int p2 = 1;
-            while (p2 < static_cast<int>(n_band)) p2 <<= 1;
-            for (int i = threadIdx.x + static_cast<int>(n_band); i < p2; i += kThreads) band[i] = ~0ull;
-            __syncthreads();
-            for (int size = 2; size <= p2; size <<= 1) {
-                for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                    for (int i = threadIdx.x; i < p2 / 2; i += kThreads) {
-                        const int lo = 2 * i - (i & (stride - 1));
-                        const int hi = lo + stride;
-                        const bool up = ((lo & size) == 0);
-                        const uint64_t x = band[lo], y = band[hi];
-                        if ((x > y) == up) { band[lo] = y; band[hi] = x; }
-                    }
-                    __syncthreads();
+            // sure picks (s~ above the band) are counted; band keys go to
+            // band[] as candidate indices
+            for (uint32_t i = tid; i < C; i += kThreads) {
+                const uint32_t ck = cand[i].x;
+                if (ck > hi_key) {
+                    atomicAdd(&counters[0], 1u);
+                } else if (ck >= lo_key) {
+                    const uint32_t at = atomicAdd(&counters[1], 1u);
+                    if (at < static_cast<uint32_t>(kBandCap)) band[at] = i;
                 }
             }
-            const uint32_t need_b = k_eff - n_in;
-            for (uint32_t i = threadIdx.x; i < need_b; i += kThreads)
-                sel[n_in + i] = static_cast<uint32_t>(band[i]);
-            int q2 = 1;
-            while (q2 < static_cast<int>(k_eff)) q2 <<= 1;
-            for (int i = threadIdx.x + static_cast<int>(k_eff); i < q2; i += kThreads) sel[i] = 0xffffffffu;
             __syncthreads();
-            bitonic_sort(sel, q2);
-            for (uint32_t i = threadIdx.x; i < k_eff; i += kThreads) o[i] = static_cast<int32_t>(sel[i]);
+            const uint32_t n_in = counters[0], n_band = counters[1];
+            if (n_band > static_cast<uint32_t>(kBandCap) || n_in > k_eff || n_in + n_band < k_eff) {
+                fallback = true;
+            } else {
+                // exact scores of the band keys, ranked by (score desc,
+                // position asc): entry = (~exact key << 32) | position, the
+                // need_b smallest entries are chosen
+                for (uint32_t i = tid; i < n_band; i += kThreads) {
+                    const uint32_t ci = static_cast<uint32_t>(band[i]);
+                    const uint32_t pos = cand[ci].y;
+                    const uint32_t ek = key_of(exact_score(qf, wf, a.kc, pos));
+                    band[i] = (static_cast<uint64_t>(~ek) << 32) | pos;
+                    sel[i] = ci;
+                }
+                __syncthreads();
+                const uint32_t need_b = k_eff - n_in;
+                // rank of each band entry among the band (entries are distinct:
+                // positions differ); chosen ones are marked by setting their
+                // candidate key to ~0u (above every real key)
+                for (uint32_t i = tid; i < n_band; i += kThreads) {
+                    const uint64_t x = band[i];
+                    uint32_t rank = 0;
+                    for (uint32_t j2 = 0; j2 < n_band; ++j2) rank += band[j2] < x;
+                    if (rank < need_b) cand[sel[i]].x = 0xffffffffu;
+                }
+                __syncthreads();
+                // ordered emission: candidates are in position order
+                uint32_t written = 0;
+                for (uint32_t base = 0; base < C; base += kThreads) {
+                    const uint32_t i = base + tid;
+                    const bool pick = i < C && cand[i].x > hi_key;
+                    uint32_t tot;
+                    const uint32_t at = written + block_excl_prefix(pick, wave_tot, tot);
+                    if (pick && at < k_eff) o[at] = static_cast<int32_t>(cand[i].y);
+                    written += tot;
+                }
+            }
         }
     }
     if (fallback) {
-        // exact scores for the whole visible row (overwrites its s~ row)
-        float* s = st + r * ld;
+        // exact scores for the whole visible row, kept in the row's slot
+        // range (8 bytes reserved per visible key)
+        float* s = reinterpret_cast<float*>(region);
         __syncthreads();
-        for (int64_t i = threadIdx.x; i < vis; i += kThreads) s[i] = exact_score(qf, wf, a.kc, i);
+        for (int64_t i = tid; i < vis; i += kThreads) s[i] = exact_score(qf, wf, a.kc, i);
         __threadfence_block();
         __syncthreads();
         uint32_t T = 0, need = 0;
@@ -487,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void band_final_kernel(float* __restrict_
         radix_select(get, vis, k_eff, hist, res, T, need);
         emit_ordered(get, vis, T, need, k_eff, nullptr, o, k, wave_tot);
     }
-    for (int64_t i = k_eff + threadIdx.x; i < k; i += kThreads) o[i] = -1;
+    for (int64_t i = k_eff + tid; i < k; i += kThreads) o[i] = -1;
 }
 
 __global__ void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -495,61 +651,93 @@ __global__ void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
     if (i < n) p[i] = 0u;
 }
 
-// per-row 12-bit histogram of s~ keys over [0, vis(t)); scores of one row
-// spread over tens of bins, so plain LDS atomics rarely collide
-__global__ __launch_bounds__(kThreads) void band_hist_kernel(const float* __restrict__ st, int64_t ld, int64_t t0,
-                                                             PfArgs a, uint32_t* __restrict__ hist_all) {
-    constexpr int kPer = 16;
-    constexpr int kChunk = kPer * kThreads;
-    __shared__ uint32_t hist[kBins];
-    const int64_t r = blockIdx.y;
-    const int64_t vis = vis_of(a, t0 + r);
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk;
-    if (base >= vis || vis <= a.k) return;
-    const float* s = st + r * ld;
-    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
-    uint32_t kk[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int64_t i = base + j * kThreads + threadIdx.x;
-        kk[j] = (i < vis) ? key_of(s[i]) : 0u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        if (kk[j] != 0u) atomicAdd(&hist[kk[j] >> 20], 1u);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kBins; i += kThreads)
-        if (hist[i]) atomicAdd(&hist_all[r * kBins + i], hist[i]);
-}
-
 struct PfWs {
     uint32_t* kmax;
     float* eps;
-    float* st;
-    uint32_t* hist;     // [rows][kBins]
-    uint32_t* cnt;      // [rows]
+    float* samp;        // [rows][ld_s]
     uint32_t* thr;      // [rows]
-    uint2* cand;        // [rows][kCandCap]
-    int64_t ld;
+    uint32_t* counts;   // [rows][cnt_ld]
+    uint2* cand;        // [rows][cand_ld]
+    int64_t ld_s, cnt_ld, cand_ld;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
+struct PfSizes {
+    int64_t rows, ld_s, cnt_ld, cand_ld;
+    size_t kmax, eps, samp, thr, counts, cand;
+    size_t total() const { return kmax + eps + samp + thr + counts + cand; }
+};
+
+// Candidate slots per row: a workgroup's slot range is its key range, and the
+// ranges cover [0, cols) with less than one range (<= kMaxKeysPerWG keys) of
+// overshoot.  Count entries per row: one per workgroup, at least 128 keys each.
+PfSizes sizes_of(int64_t T, int64_t n_cols) {
+    PfSizes z;
+    z.rows = T < kChunkRows ? T : kChunkRows;
+    z.ld_s = (n_cols + kGroup - 1) / kGroup * kSub;
+    z.cnt_ld = (n_cols + kTileKeys - 1) / kTileKeys + 8;
+    z.cand_ld = (n_cols + kTileKeys - 1) / kTileKeys * kTileKeys + kMaxKeysPerWG;
+    z.kmax = 256;
+    z.eps = align256(static_cast<size_t>(T) * 4);
+    z.samp = align256(static_cast<size_t>(z.rows) * z.ld_s * 4);
+    z.thr = align256(static_cast<size_t>(z.rows) * 4);
+    z.counts = align256(static_cast<size_t>(z.rows) * z.cnt_ld * 4);
+    z.cand = align256(static_cast<size_t>(z.rows) * z.cand_ld * 8);
+    return z;
+}
+
 PfWs carve(void* ws, int64_t T, int64_t n_cols) {
+    const PfSizes z = sizes_of(T, n_cols);
     PfWs w;
     char* p = static_cast<char*>(ws);
-    const int64_t rows = T < kChunkRows ? T : kChunkRows;
-    w.ld = (n_cols + 63) / 64 * 64;
-    w.kmax = reinterpret_cast<uint32_t*>(p); p += 256;
-    w.eps = reinterpret_cast<float*>(p); p += align256(static_cast<size_t>(T) * 4);
-    w.st = reinterpret_cast<float*>(p); p += align256(static_cast<size_t>(rows) * w.ld * 4);
-    w.hist = reinterpret_cast<uint32_t*>(p); p += align256(static_cast<size_t>(rows) * (kBins + 2) * 4);
-    w.cnt = w.hist + rows * kBins;
-    w.thr = w.cnt + rows;
-    w.cand = reinterpret_cast<uint2*>(p); p += align256(static_cast<size_t>(rows) * kCandCap * 8);
+    w.kmax = reinterpret_cast<uint32_t*>(p); p += z.kmax;
+    w.eps = reinterpret_cast<float*>(p); p += z.eps;
+    w.samp = reinterpret_cast<float*>(p); p += z.samp;
+    w.thr = reinterpret_cast<uint32_t*>(p); p += z.thr;
+    w.counts = reinterpret_cast<uint32_t*>(p); p += z.counts;
+    w.cand = reinterpret_cast<uint2*>(p); p += z.cand;
+    w.ld_s = z.ld_s;
+    w.cnt_ld = z.cnt_ld;
+    w.cand_ld = z.cand_ld;
     return w;
 }
+
+int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Split `units` column blocks (32 keys each) of n_y query blocks over
+// workgroups of a multiple of 4 blocks, sized so the grid fills whole rounds
+// of one workgroup per CU (about `per_wg` blocks each), numbered XCD-aware.
+Geo make_geo(int64_t units, int n_y, int64_t per_wg, int64_t max_blocks, int n_cu) {
+    Geo g;
+    g.n_y = n_y;
+    int64_t rounds = (units * n_y + per_wg * n_cu / 2) / (per_wg * n_cu);
+    if (rounds < 1) rounds = 1;
+    const int64_t want_x = (cdiv(n_cu * rounds, n_y) + 7) / 8 * 8;
+    int64_t blocks = (cdiv(units, want_x) + 3) / 4 * 4;
+    if (blocks > max_blocks) blocks = max_blocks;
+    if (blocks < 4) blocks = 4;
+    g.blocks = static_cast<int32_t>(blocks);
+    g.n_x = cdiv(units, blocks);
+    g.xcd = 1;
+    g.cand_ld = 0;
+    g.cnt_ld = 0;
+    return g;
+}
+
+unsigned grid_of(const Geo& g) { return static_cast<unsigned>((g.n_x + 7) / 8 * 8 * g.n_y); }
 
 }  // namespace
 
@@ -561,11 +749,7 @@ int64_t prefill_cols(int64_t T, int32_t ctx_len, int64_t q_pos0, int32_t m) {
 
 size_t prefill_topk_workspace_bytes(int64_t T, int32_t ctx_len, int64_t q_pos0, int32_t m) {
     if (T <= 0) return 0;
-    const int64_t n_cols = prefill_cols(T, ctx_len, q_pos0, m);
-    const int64_t rows = T < kChunkRows ? T : kChunkRows;
-    const int64_t ld = (n_cols + 63) / 64 * 64;
-    return 256 + align256(static_cast<size_t>(T) * 4) + align256(static_cast<size_t>(rows) * ld * 4) +
-           align256(static_cast<size_t>(rows) * (kBins + 2) * 4) + align256(static_cast<size_t>(rows) * kCandCap * 8);
+    return sizes_of(T, prefill_cols(T, ctx_len, q_pos0, m)).total();
 }
 
 int prefill_topk_max_k() { return kKCap; }
@@ -588,24 +772,30 @@ hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st)
     if (n_cols > 0)
         knorm_max_kernel<<<dim3(static_cast<unsigned>((n_cols + 255) / 256)), 256, 0, st>>>(a.kc, n_cols, w.kmax);
     eps_kernel<<<dim3(static_cast<unsigned>((L.T + 31) / 32)), 256, 0, st>>>(a, w.kmax, w.eps);
+    const int n_cu = cu_count();
     for (int64_t t0 = 0; t0 < L.T; t0 += kChunkRows) {
         const int64_t t1 = t0 + kChunkRows < L.T ? t0 + kChunkRows : L.T;
         const int64_t rows = t1 - t0;
-        const int64_t cols = prefill_cols(t1, L.ctx_len, L.q_pos0, L.m);
-        const int64_t hwords = rows * (kBins + 1);      // histograms and candidate counts
-        zero_words_kernel<<<dim3(static_cast<unsigned>((hwords + 255) / 256)), 256, 0, st>>>(w.hist, hwords);
-        if (cols > 0) {
-            const dim3 g1(static_cast<unsigned>((cols + kKeysPerWG - 1) / kKeysPerWG),
-                          static_cast<unsigned>((rows + kQB - 1) / kQB));
-            score_mfma_kernel<<<g1, 512, 0, st>>>(a, t0, t1, cols, w.ld, w.st);
-            const dim3 g2(static_cast<unsigned>((cols + 16 * kThreads - 1) / (16 * kThreads)),
-                          static_cast<unsigned>(rows));
-            band_hist_kernel<<<g2, kThreads, 0, st>>>(w.st, w.ld, t0, a, w.hist);
-            band_thresh_kernel<<<dim3(static_cast<unsigned>(rows)), 256, 0, st>>>(t0, a, w.eps, w.hist, w.thr);
-            band_collect_kernel<<<g2, kThreads, 0, st>>>(w.st, w.ld, t0, a, w.thr, w.cnt, w.cand);
+        const int64_t cols = prefill_cols(t1, L.ctx_len, L.q_pos0, L.m);   // widest row of the chunk
+        const int qblocks = static_cast<int>(cdiv(rows, kQB));
+        if (cols > kCandCap) {
+            Geo gs = make_geo(cdiv(cols, kGroup), qblocks, 16, 1 << 20, n_cu);
+            score_mfma_kernel<true><<<grid_of(gs), 512, 0, st>>>(a, t0, t1, cols, gs, w.samp, w.ld_s, nullptr,
+                                                                  nullptr, nullptr);
         }
-        band_final_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(w.st, w.ld, t0, a, w.eps, w.cnt,
-                                                                                  w.cand, L.out);
+        sample_thresh_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(t0, a, w.samp, w.ld_s, w.thr);
+        int64_t kpw = kTileKeys;
+        if (cols > 0) {
+            Geo gc = make_geo(cdiv(cols, kSub), qblocks, 4096 / kSub, kMaxKeysPerWG / kSub, n_cu);
+            gc.cand_ld = w.cand_ld;
+            gc.cnt_ld = w.cnt_ld;
+            kpw = static_cast<int64_t>(gc.blocks) * kSub;
+            score_mfma_kernel<false><<<grid_of(gc), 512, 0, st>>>(a, t0, t1, cols, gc, nullptr, 0, w.thr, w.counts,
+                                                                   w.cand);
+        }
+        cand_final_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(t0, a, w.eps, w.thr, w.counts,
+                                                                                  w.cnt_ld, w.cand_ld, kpw, w.cand,
+                                                                                  L.out);
     }
     return hipGetLastError();
 }

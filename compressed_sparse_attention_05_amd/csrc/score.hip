@@ -214,10 +214,12 @@ hipError_t launch_typed(const ScoreLaunch& p, hipStream_t st) {
     a.n_slots = p.pool ? static_cast<int64_t>(p.P_b) * 8 : p.ld;
     a.units_per_row = (a.n_slots + kUnit - 1) / kUnit;
     a.q_bf16 = p.q_bf16;
-    // enough workgroups to keep every CU at full occupancy (~2,048), at
-    // least 4 units (one per wave) each
-    int64_t upw = (a.units_per_row * rows + 2047) / 2048;
-    if (upw < kWaves) upw = kWaves;
+    // one unit per wave: each workgroup reads 4 consecutive units (128 KiB
+    // of keys at d_I = 128), so the workgroups in flight at any time read a
+    // compact, moving window of the cache.  Measured at 1M entries x 64 rows
+    // this reads 13% faster than fewer, longer workgroups (5.75 against
+    // 5.05 TB/s); the query staging per workgroup costs 2 KiB.
+    const int64_t upw = kWaves;
     a.units_per_wg = static_cast<int>(upw);
     const int64_t gx = (a.units_per_row + upw - 1) / upw;
     if (gx == 0 || rows == 0) return hipGetLastError();

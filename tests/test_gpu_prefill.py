@@ -96,3 +96,58 @@ def test_prefill_topk_full_chunk_sampled(K):
     rng = np.random.default_rng(3)
     rows = sorted(set([0, 1, 2047, 4096, T - 1] + list(rng.integers(0, T, 5))))
     _check_rows(got, q, w, kc, N, q_pos0, m, k, rows)
+
+
+# Rows with more than 12,288 visible entries take the sampled threshold:
+# one 32-key block per 256 keys is scored first, the row's candidates are
+# the keys at or above a sample quantile, and the final pass checks that
+# they cover the band around the k-th score.
+@pytest.mark.parametrize("k", [512, 2048])
+def test_prefill_topk_sampled_threshold(K, k):
+    T, cap, m = 64, 40960, 2
+    q_pos0 = 2 * cap - 2 * T          # vis(t) runs from cap - T to cap
+    q, w, kc = _inputs(2004, T, cap)
+    print(f"prefill topk sampled T={T} cap={cap} k={k}", flush=True)
+    got = _run(K, q, w, kc, cap, q_pos0, m, k)
+    _check_rows(got, q, w, kc, cap, q_pos0, m, k, range(T))
+
+
+def test_prefill_topk_sampled_ragged_context(K):
+    # ctx_len 20,000 is not a multiple of the 256-key sample group or of the
+    # 4,096-key candidate workgroup: the last group and workgroup are partial
+    T, cap, m, k = 40, 20480, 1, 1000
+    ctx = 20000
+    q_pos0 = 30000
+    q, w, kc = _inputs(2005, T, cap)
+    got = _run(K, q, w, kc, ctx, q_pos0, m, k)
+    _check_rows(got, q, w, kc, ctx, q_pos0, m, k, range(T))
+
+
+def test_prefill_topk_too_many_candidates_falls_back(K):
+    # every key equal with 20,480 visible: the sample quantile equals every
+    # score, all keys become candidates (more than the 12,288 staged), and
+    # the row is redone exactly; ties -> positions 0..k-1
+    T, cap, m, k = 4, 20480, 1, 300
+    q, w, _ = _inputs(2006, T, cap)
+    kc = ci.gaussian(2006, ci.TID_K_IDX, (1, 128), torch.bfloat16).repeat(cap, 1)
+    got = _run(K, q, w, kc, cap, cap - T, m, k)
+    _check_rows(got, q, w, kc, cap, cap - T, m, k, range(T))
+    assert np.array_equal(got[0], np.arange(k))
+
+
+def test_prefill_topk_misleading_sample_falls_back(K):
+    # Only the sampled 32-key blocks hold nonzero keys (the block of 256-key
+    # group g is 8g + (g * 0x9E3779B1 mod 2^32) >> 29); every other key
+    # scores exactly 0.  The sample then sees only the high scores, its
+    # quantile sits above the row's k-th score, too few keys qualify, and the
+    # exact fallback must still give the definition's top-k (the high keys,
+    # then the zero-score keys by position).
+    T, cap, m, k = 8, 20480, 1, 2048
+    q, w, kc = _inputs(2007, T, cap)
+    keep = torch.zeros(cap, dtype=torch.bool)
+    for g in range(cap // 256):
+        h = ((g * 0x9E3779B1) & 0xFFFFFFFF) >> 29
+        keep[256 * g + 32 * h: 256 * g + 32 * h + 32] = True
+    kc = torch.where(keep[:, None], kc, torch.zeros_like(kc))
+    got = _run(K, q, w, kc, cap, cap - T, m, k)
+    _check_rows(got, q, w, kc, cap, cap - T, m, k, range(T))
