@@ -512,14 +512,17 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
 //   S-waves 0..3 (head group hg = w & 1, key block kb = w >> 1): S^T for 32
 //     keys x 32 heads over all 512 channels (32 MFMAs, q in registers), the
 //     online softmax of that block and its P fragments;
-//   D-waves 4..7 (channel slice dw = w - 4): gather and dequantise the next
-//     tile into the other Kt buffer (16 keys each), and O^T[128 d][64 heads]
-//     += V^T P^T with V^T read transposed from Kt.
-// Per tile two phases separated by barriers:
+//   D-waves 4..7 (channel slice dw = w - 4): O^T[128 d][64 heads] += V^T P^T
+//     with V^T read transposed from Kt.
+// Every wave gathers and dequantises 8 keys (8w .. 8w + 7) of the next tile
+// into the other Kt buffer.  Per tile two phases separated by barriers:
 //   phase 1: S-waves S(i) and their block max   || D-waves P.V(i - 1)
-//   phase 2: S-waves softmax(i) -> P, rescale   || D-waves dequant(i + 1)
+//   phase 2: S-waves softmax(i) -> P, rescale; then all waves dequant(i + 1)
+//            and issue the gathers of tile i + 2
 // so the matrix cores of every SIMD get work from both roles and no S
-// partial sums cross waves (each S-wave covers all channels).
+// partial sums cross waves (each S-wave covers all channels).  The gathers
+// are buffer loads whose row offset is a scalar, so a key costs no vector
+// address arithmetic; rows beyond the cache read zeros.
 template <bool BF16>
 __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     constexpr int D = 512, KT = 64, KROW = D + 8, SSTEPS = D / 16;
@@ -623,43 +626,74 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     }
 
     // ---- D-wave state: O^T accumulator (d tile mt, head tile nt) is
-    // R[2mt + nt]; the gathered rows of the next main tile (keys 16dw + i,
-    // channels 8lane..) wait in pm_*
-    uint32_t pm_cw[16], pm_sc[16];
-    uint32_t pm_ok = 0;
+    // R[2mt + nt].  Every wave gathers 8 keys (8w .. 8w + 7) of the next main
+    // tile in two groups of 4: lane l takes key 4g + l/16 of the group and
+    // its channels 32(l%16) .. +31 (16 code bytes and 2 scale bytes), so a
+    // group is one 16-byte load and one 2-byte load per lane.
+    constexpr int KPW = KT / 8;                       // keys gathered per wave
+    uint4 pm_c[2];
+    uint32_t pm_s[2];
+    uint32_t pm_ok = 0;                               // bit g: this lane's key of group g is a real row
+    // buffer resources over this unit's rows (offsets fit 32 bits when the
+    // cache has fewer than 2^31 / 256 rows; larger caches use global loads)
+    const bool use_buf = a.cap * (D / 2) <= 0x7fffffffLL;
+    const __amdgpu_buffer_rsrc_t rc_codes = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.codes + kvbase * (D / 2)), static_cast<short>(0),
+        use_buf ? static_cast<int>(a.cap * (D / 2)) : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc_scales = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.scales + kvbase * (D / 16)), static_cast<short>(0),
+        use_buf ? static_cast<int>(a.cap * (D / 16)) : 0, 0x00020000);
+    const int gpart = lane & 15, gkey = lane >> 4;
     auto prefetch_main = [&](int tile) {
         pm_ok = 0;
-        // lane i < 16 fetches the index of key 16dw + i; each key's row then
-        // comes out of that lane as a scalar
-        const int32_t rows16 = idx_s[tile * KT + 16 * dw + (lane & 15) - win0 * KT];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int32_t row = __builtin_amdgcn_readlane(rows16, i);
+        for (int g = 0; g < 2; ++g) {
+            const int key = KPW * wv + 4 * g + gkey;
+            const int32_t row = idx_s[tile * KT + key - win0 * KT];
             const bool ok = row >= 0 && row < a.cap;
-            const int64_t rr = kvbase + (ok ? row : 0);
-            pm_ok |= ok ? (1u << i) : 0u;
-            pm_cw[i] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * lane);
-            pm_sc[i] = a.scales[rr * (D / 16) + (lane >> 1)];
+            const int32_t rw = ok ? row : 0;
+            pm_ok |= ok ? (1u << g) : 0u;
+            if (use_buf) {
+                pm_c[g] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rc_codes, rw * (D / 2) + 16 * gpart, 0, 0));
+                pm_s[g] = __builtin_amdgcn_raw_buffer_load_b16(rc_scales, rw * (D / 16) + 2 * gpart, 0, 0);
+            } else {
+                const int64_t rr = kvbase + rw;
+                pm_c[g] = *reinterpret_cast<const uint4*>(a.codes + rr * (D / 2) + 16 * gpart);
+                pm_s[g] = *reinterpret_cast<const uint16_t*>(a.scales + rr * (D / 16) + 2 * gpart);
+            }
         }
     };
+    // one key row (all lanes, 8 channels each); every lane writes the mask
+    // entry (the same value), so the write needs no branch
     auto store_key = [&](int buf, int key, const uint32_t (&h)[4], bool valid) {
         *reinterpret_cast<uint4*>(&Kt[buf][key * KROW + 8 * lane]) = make_uint4(h[0], h[1], h[2], h[3]);
-        if (lane == 0) kmask[buf][key] = valid ? 0.0f : -__builtin_inff();
+        kmask[buf][key] = valid ? 0.0f : -__builtin_inff();
     };
     auto dequant_prefetched = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t h[4];
-            dequant8_hw(pm_cw[i], pm_sc[i], h);
+        for (int g = 0; g < 2; ++g) {
+            const int key = KPW * wv + 4 * g + gkey;
+            const uint32_t cw[4] = {pm_c[g].x, pm_c[g].y, pm_c[g].z, pm_c[g].w};
+            _Float16* dst = &Kt[buf][key * KROW + 32 * gpart];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // rotate the 16-byte pieces by the lane so neighbouring lanes
+                // write different banks
+                const int ee = (e + gpart) & 3;
+                uint32_t h[4];
+                dequant8_hw(cw[ee], (pm_s[g] >> (8 * (ee >> 1))) & 0xffu, h);
+                *reinterpret_cast<uint4*>(dst + 8 * ee) = make_uint4(h[0], h[1], h[2], h[3]);
+            }
             // an empty slot keeps the finite values of the clamped row; its
             // logit is -inf, so it enters P.V with weight exactly 0
-            store_key(buf, 16 * dw + i, h, (pm_ok >> i) & 1u);
+            kmask[buf][key] = ((pm_ok >> g) & 1u) ? 0.0f : -__builtin_inff();
         }
     };
     // any tile (main rows, window rows, empty slots), loaded and stored at once
     auto load_generic = [&](int tile, int buf) {
-        for (int i = 0; i < 16; ++i) {
-            const int key = 16 * dw + i;
+        for (int i = 0; i < KPW; ++i) {
+            const int key = KPW * wv + i;
             const int slot = tile * KT + key;
             uint32_t h[4] = {0u, 0u, 0u, 0u};
             bool valid = false;
@@ -731,7 +765,7 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
 
     if (tid < 2) grow_s[tid] = 0;
     __syncthreads();                                  // idx_s staged
-    if (!s_role && n_it > 0) {
+    if (n_it > 0) {
         if (t_begin < t_main_end) {
             prefetch_main(t_begin);
             dequant_prefetched(0);
@@ -822,7 +856,8 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             l_run += psum;
             Pb[hg][2 * kb][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
             Pb[hg][2 * kb + 1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-        } else if (tile + 1 < t_end) {
+        }
+        if (tile + 1 < t_end) {
             if (tile + 1 < t_main_end) dequant_prefetched(buf ^ 1);
             else load_generic(tile + 1, buf ^ 1);
             if (tile + 2 < t_end && tile + 2 < t_main_end) prefetch_main(tile + 2);
