@@ -1015,9 +1015,46 @@ SplitPlan plan(int64_t units, int H, int k, int W, int KT) {
     return p;
 }
 
+// The warp-specialised kernel runs one 512-thread workgroup per CU (its LDS
+// use), so its key splits are chosen by rounds of kCUs workgroups: the cost
+// of a plan is (rounds) x (tiles per split + about 2 tiles of start-up and
+// write-out) plus the combine's reading of the partials.  Fixed at the
+// MI355X CU count, so the workspace size never depends on the device.
+constexpr int kCUs = 256;
+bool use_ws(int64_t units, int D) { return D == 512 && units >= 64; }
+
+SplitPlan plan_ws(int64_t units, int H, int k, int W, int KT) {
+    SplitPlan best;
+    best.n_tiles = (k + W + KT - 1) / KT;
+    const int64_t hblocks = (H + 63) / 64;
+    const int min_tiles = 128 / KT;
+    int max_splits = (best.n_tiles + min_tiles - 1) / min_tiles;
+    if (max_splits > kCombineMaxSplits) max_splits = kCombineMaxSplits;
+    if (max_splits < 1) max_splits = 1;
+    double best_cost = 1e300;
+    best.splits = 1;
+    best.tiles_per_split = best.n_tiles > 0 ? best.n_tiles : 1;
+    for (int s = 1; s <= max_splits; ++s) {
+        const int tps = (best.n_tiles + s - 1) / s;
+        if (tps < 1) break;
+        const int se = (best.n_tiles + tps - 1) / tps;
+        const int64_t wgs = units * hblocks * se;
+        const int64_t rounds = (wgs + kCUs - 1) / kCUs;
+        const double cost = static_cast<double>(rounds) * (tps + 2) +
+                            (se > 1 ? 0.5 * static_cast<double>(wgs) / kCUs : 0.0);
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best.splits = se;
+            best.tiles_per_split = tps;
+        }
+    }
+    return best;
+}
+
 template <int D, int NQ, bool BF16>
 hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
-    const SplitPlan sp = plan(L.units, L.H, L.k, L.W, tile_keys(D));
+    const SplitPlan sp = use_ws(L.units, D) ? plan_ws(L.units, L.H, L.k, L.W, tile_keys(D))
+                                            : plan(L.units, L.H, L.k, L.W, tile_keys(D));
     const int hblocks = (L.H + 63) / 64;
     AttnArgs a;
     a.q = static_cast<const uint16_t*>(L.q); a.q_bf16 = L.q_bf16;
@@ -1035,7 +1072,7 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     // many query units (prefill chunks, large batches): the warp-specialised
     // kernel keeps the matrix cores busier; few units: the split kernel has
     // the shorter start-up
-    if (D == 512 && L.units >= 64)
+    if (use_ws(L.units, D))
         attn_ws_kernel<BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 512, 0, st>>>(a);
     else
         attn_kernel<D, NQ, BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 128 * NQ, 0, st>>>(a);
@@ -1053,7 +1090,7 @@ bool attn_shape_supported(int H, int D) {
 }
 
 size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W) {
-    const SplitPlan sp = plan(units, H, k, W, tile_keys(D));
+    const SplitPlan sp = use_ws(units, D) ? plan_ws(units, H, k, W, tile_keys(D)) : plan(units, H, k, W, tile_keys(D));
     if (sp.splits == 1) return 0;
     const int64_t hblocks = (H + 63) / 64;
     const int64_t nparts = units * hblocks * sp.splits;

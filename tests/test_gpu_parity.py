@@ -367,10 +367,13 @@ def test_attention_prefill_window(K):
         assert err < ATOL
 
 
-def test_attention_prefill_long_split_sampled(K):
-    """Enough query units that each workgroup walks all 68 key tiles of a
-    query (index list restaged in windows); sampled queries vs the oracle."""
-    T, N, D, H, k, W = 520, 40000, 512, 64, 2048, 128
+@pytest.mark.parametrize("T", [520, 1024])
+def test_attention_prefill_long_split_sampled(K, T):
+    """Many query units on the warp-specialised kernel: 520 units take two
+    key splits per query; 1,024 units take one, so each workgroup walks all
+    34 key tiles of its query (index list restaged in windows) and writes
+    the output directly.  Sampled queries vs the oracle."""
+    N, D, H, k, W = 40000, 512, 64, 2048, 128
     seed = 302
     kv = ci.gaussian(seed, ci.TID_KV, (N, D), dtype=torch.float32)
     codes, scales = oracle.mxfp4_encode(kv)
@@ -383,7 +386,7 @@ def test_attention_prefill_long_split_sampled(K):
     out = K.csa2_sparse_attn_prefill(dev(q), dev(torch.from_numpy(codes)), dev(torch.from_numpy(scales)),
                                      dev(idx), dev(swa), W, q_pos0).cpu().numpy()
     errs = []
-    for t in (0, 7, 100, 333, 519):
+    for t in (0, 7, 100, 333, T - 1):
         want = oracle.attn_prefill(q[t:t + 1], codes, scales, idx[t:t + 1].numpy(), swa[t:t + W], W,
                                    q_pos0 + t, 0, 1 / math.sqrt(D))
         errs.append(np.max(np.abs(out[t] - want[0])))
