@@ -62,6 +62,7 @@ SIGNATURES = {
     "csa2_build_candidate_pool_workspace_size": (ctypes.c_size_t, [i64, i64, i32]),
     "csa2_build_candidate_pool": (ctypes.c_int, [P, i64, i64, i64, i32, P, P, ctypes.c_size_t, P]),
     "csa2_topk_from_pool": (ctypes.c_int, [P, i64, i64, P, i32, i32, P, P]),
+    "csa2_pool_topk": (ctypes.c_int, [P, i64, i64, i64, i32, P, P, i64, i32, P, P]),
     "csa2_sparse_attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), P, ctypes.c_size_t, P]),
     "csa2_sparse_attn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnPrefillArgs)]),
@@ -264,6 +265,24 @@ def csa2_topk_from_pool(scores, pool_blocks, k: int, *, out=None, stream=None):
     _check(lib().csa2_topk_from_pool(_ptr(scores), rows, ld, _ptr(pool_blocks), P_b, k, _ptr(out),
                                      _stream(stream)))
     return out
+
+
+def csa2_pool_topk(block_max, scores, P_b: int, k: int, n_blocks: Optional[int] = None, *,
+                   out_blocks=None, out=None, stream=None):
+    """Candidate pool [..., P_b] and Full-mode top-k [..., k] in one launch;
+    the same results as csa2_build_candidate_pool then csa2_topk_from_pool."""
+    _dev(block_max, "block_max"); _dev(scores, "scores")
+    ld_bm = block_max.shape[-1]
+    ld = scores.shape[-1]
+    rows = scores.numel() // ld if ld else 0
+    nb = ld_bm if n_blocks is None else n_blocks
+    if out_blocks is None:
+        out_blocks = torch.empty((*scores.shape[:-1], P_b), dtype=torch.int32, device=scores.device)
+    if out is None:
+        out = torch.empty((*scores.shape[:-1], k), dtype=torch.int32, device=scores.device)
+    _check(lib().csa2_pool_topk(_ptr(block_max), rows, nb, ld_bm, P_b, _ptr(out_blocks), _ptr(scores), ld, k,
+                                _ptr(out), _stream(stream)))
+    return out_blocks, out
 
 
 def csa2_sparse_attn_decode(q, codes, scales, idx, swa, swa_len, *, sm_scale: Optional[float] = None,

@@ -184,6 +184,25 @@ int csa2_topk_from_pool(const float* scores, int64_t rows, int64_t ld, const int
                          "csa2_topk_from_pool");
 }
 
+int csa2_pool_topk(const float* block_max, int64_t rows, int64_t n_blocks, int64_t ld_bm, int32_t P_b,
+                   int32_t* out_blocks, const float* scores, int64_t ld, int32_t k, int32_t* out_idx,
+                   void* stream) {
+    if (rows < 0 || n_blocks < 0 || ld_bm < n_blocks || ld < 0)
+        return fail(CSA2_E_INVALID, "csa2_pool_topk: need rows >= 0, 0 <= n_blocks <= ld_bm, ld >= 0");
+    if (k <= 0 || P_b <= 0 || k > P_b)
+        return fail(CSA2_E_INVALID, "csa2_pool_topk: need 0 < k <= P_b (the pool holds the top-k only then)");
+    if (!csa2::pool_topk_supported(n_blocks, P_b, k))
+        return fail(CSA2_E_UNSUPPORTED,
+                    "csa2_pool_topk: P_b=%d, n_blocks=%lld outside the one-workgroup path (P_b <= 2048, "
+                    "n_blocks <= 32,768): call csa2_build_candidate_pool and csa2_topk_from_pool",
+                    P_b, static_cast<long long>(n_blocks));
+    if (rows == 0) return ok();
+    if (!block_max || !out_blocks || !scores || !out_idx) return fail(CSA2_E_INVALID, "csa2_pool_topk: null pointer");
+    return device_status(csa2::launch_pool_topk(block_max, rows, n_blocks, ld_bm, P_b, out_blocks, scores, ld, k,
+                                                out_idx, as_stream(stream)),
+                         "csa2_pool_topk");
+}
+
 // --------------------------------------------------------------------------
 static int check_attn_common(const char* fn, const void* q, int q_dtype, const uint8_t* codes,
                              const uint8_t* scales, int64_t cap, const int32_t* idx, int32_t k,

@@ -39,6 +39,9 @@ hipError_t launch_topk_from_pool(const float* scores, int64_t rows, int64_t ld, 
 bool pool_in_lds(int64_t n_blocks, int P_b);
 hipError_t launch_pool(const float* bmax, int64_t rows, int64_t n_blocks, int64_t ld, int P_b, int32_t* out,
                        hipStream_t st);
+bool pool_topk_supported(int64_t n_blocks, int P_b, int k);
+hipError_t launch_pool_topk(const float* bmax, int64_t rows, int64_t n_blocks, int64_t ld_bm, int P_b,
+                            int32_t* pool, const float* scores, int64_t ld, int k, int32_t* out, hipStream_t st);
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int k,
                        const int32_t* pool, int P_b, int32_t* out, void* ws, hipStream_t st);
 

@@ -531,7 +531,87 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float* __res
     for (int64_t i = k_eff + threadIdx.x; i < k; i += kThreads) o[i] = -1;
 }
 
+// The Full layer's pool and its top-k in one workgroup per row: the pool is
+// written out (for the Reindex layers) and kept in LDS, and the top-k is then
+// selected among the pool's 8*P_b scores (the identity behind
+// topk_from_pool_kernel).  Direct pool only (n_blocks <= kSelMax); R1 keys
+// per thread for the pool selection, R2 for the top-k.
+template <int R1, int R2>
+__global__ __launch_bounds__(kThreads) void pool_topk_kernel(const float* __restrict__ bmax, int64_t n_blocks,
+                                                             int64_t ld_bm, int P_b, int32_t* __restrict__ pool,
+                                                             const float* __restrict__ scores, int64_t ld,
+                                                             int k, int32_t* __restrict__ out) {
+    __shared__ SelLds sh;
+    __shared__ int32_t pool_s[kPoolMax];
+    const int64_t row = blockIdx.x;
+    {
+        const float* bm = bmax + row * ld_bm;
+        int32_t* po = pool + row * static_cast<int64_t>(P_b);
+        const int64_t r0 = static_cast<int64_t>(threadIdx.x) * R1;
+        uint32_t kk[R1];
+        load_run_keys<R1>(bm, r0, n_blocks, kk);
+        const uint32_t got = select_run<R1>(kk, static_cast<uint32_t>(P_b), sh, [&](uint32_t r, int j) {
+            po[r] = static_cast<int32_t>(r0) + j;
+            pool_s[r] = static_cast<int32_t>(r0) + j;
+        });
+        for (int i = static_cast<int>(got) + threadIdx.x; i < P_b; i += kThreads) {
+            po[i] = -1;
+            pool_s[i] = -1;
+        }
+    }
+    __syncthreads();
+    const float* s = scores + row * ld;
+    int32_t* o = out + row * static_cast<int64_t>(k);
+    const bool aligned = (reinterpret_cast<uintptr_t>(s) & 31u) == 0;
+    constexpr int NB = R2 / 8;
+    const int b0 = threadIdx.x * NB;
+    int32_t blk[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) blk[q] = (b0 + q < P_b) ? pool_s[b0 + q] : -1;
+    uint32_t kk[R2];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        const int64_t p0 = static_cast<int64_t>(blk[q]) * 8;
+        if (blk[q] >= 0 && aligned && p0 + 8 <= ld) {
+            const float4 v0 = *reinterpret_cast<const float4*>(s + p0);
+            const float4 v1 = *reinterpret_cast<const float4*>(s + p0 + 4);
+            kk[8 * q + 0] = key_of(v0.x); kk[8 * q + 1] = key_of(v0.y);
+            kk[8 * q + 2] = key_of(v0.z); kk[8 * q + 3] = key_of(v0.w);
+            kk[8 * q + 4] = key_of(v1.x); kk[8 * q + 5] = key_of(v1.y);
+            kk[8 * q + 6] = key_of(v1.z); kk[8 * q + 7] = key_of(v1.w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                kk[8 * q + e] = (blk[q] >= 0 && p0 + e < ld) ? key_of(s[p0 + e]) : 0u;
+        }
+    }
+    const uint32_t got = select_run<R2>(kk, static_cast<uint32_t>(k), sh, [&](uint32_t r, int j) {
+        o[r] = blk[j >> 3] * 8 + (j & 7);
+    });
+    for (int i = static_cast<int>(got) + threadIdx.x; i < k; i += kThreads) o[i] = -1;
+}
+
 }  // namespace
+
+bool pool_topk_supported(int64_t n_blocks, int P_b, int k) {
+    return P_b <= kPoolMax && n_blocks <= kSelMax && k >= 1 && k <= P_b && 8 * static_cast<int64_t>(P_b) <= kSelMax;
+}
+
+hipError_t launch_pool_topk(const float* bmax, int64_t rows, int64_t n_blocks, int64_t ld_bm, int P_b,
+                            int32_t* pool, const float* scores, int64_t ld, int k, int32_t* out, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(rows));
+    const bool r1_16 = n_blocks <= 16 * kThreads, r2_16 = 8 * P_b <= 16 * kThreads;
+    if (r1_16 && r2_16)
+        pool_topk_kernel<16, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+    else if (r1_16)
+        pool_topk_kernel<16, 32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+    else if (r2_16)
+        pool_topk_kernel<32, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+    else
+        pool_topk_kernel<32, 32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk_from_pool(const float* scores, int64_t rows, int64_t ld, const int32_t* pool, int P_b,
                                  int k, int32_t* out, hipStream_t st) {

@@ -109,8 +109,17 @@ class DecodeStep:
                 self._keep += [sa, ws]
                 self.calls.append((f"score{li}", self.L.csa2_index_score,
                                    (ctypes.byref(sa), bd._ptr(ws), nws, None)))
+                fused = False
                 if want_bm:
                     nb = (cap + 7) // 8
+                    fused = k <= P_b <= 2048 and nb <= 32768
+                if fused:
+                    # pool and the Full top-k inside it in one launch
+                    self.calls.append((f"pool{li}", self.L.csa2_pool_topk,
+                                       (bd._ptr(self.block_max), B, nb, nb, P_b, bd._ptr(self.pool),
+                                        bd._ptr(self.scores), cap, k, bd._ptr(idx), None)))
+                    pool_built = True
+                elif want_bm:
                     pws_n = self.L.csa2_build_candidate_pool_workspace_size(B, nb, P_b)
                     pws = torch.empty(max(pws_n, 256), dtype=torch.uint8, device=dev)
                     self._keep.append(pws)
@@ -118,7 +127,9 @@ class DecodeStep:
                                        (bd._ptr(self.block_max), B, nb, nb, P_b,
                                         bd._ptr(self.pool), bd._ptr(pws), pws_n, None)))
                     pool_built = True
-                if mode == "F" and pool_built and k <= P_b and 8 * P_b <= 32768:
+                if fused:
+                    pass
+                elif mode == "F" and pool_built and k <= P_b and 8 * P_b <= 32768:
                     # the Full top-k lies inside the pool: select among its 8*P_b scores
                     self.calls.append((f"topk{li}", self.L.csa2_topk_from_pool,
                                        (bd._ptr(self.scores), B, cap, bd._ptr(self.pool), P_b, k,

@@ -187,6 +187,23 @@ int csa2_topk_from_pool(const float *scores, int64_t rows, int64_t ld, const int
                         int32_t P_b, int32_t k, int32_t *out_idx, void *stream);
 
 /* ------------------------------------------------------------------------
+ * csa2_pool_topk - csa2_build_candidate_pool followed by csa2_topk_from_pool
+ * in one launch ([KVC] section 3: the first Full layer scores every
+ * position and builds the pool in the same pass).  Same outputs, bit for
+ * bit, as the two calls: out_blocks [rows][P_b] as csa2_build_candidate_pool
+ * writes it, out_idx [rows][k] as csa2_topk_from_pool writes it.  The pool
+ * stays on chip between the two selections, so one workgroup per row does
+ * both.  Requires 0 < k <= P_b <= 2048 and n_blocks <= 32,768 (the pool
+ * selected directly, without super-blocks); other sizes return
+ * CSA2_E_UNSUPPORTED and the two calls remain.
+ * block_max [rows][ld_bm]; scores [rows][ld] (position order, -inf where
+ * invisible).  No workspace.
+ * ------------------------------------------------------------------------ */
+int csa2_pool_topk(const float *block_max, int64_t rows, int64_t n_blocks, int64_t ld_bm, int32_t P_b,
+                   int32_t *out_blocks, const float *scores, int64_t ld, int32_t k, int32_t *out_idx,
+                   void *stream);
+
+/* ------------------------------------------------------------------------
  * csa2_sparse_attn_decode - gather, dequantise, join with SWA, attend
  * ([DR] 03; [THR] post 4).  For each sequence b and head h:
  *   rows  = [MXFP4 main rows idx[b][j] (j < k, entries -1 skipped)]

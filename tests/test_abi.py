@@ -94,7 +94,7 @@ def test_prefill_topk_argument_checks():
     a = binding.PrefillTopkArgs(q_idx=256, q_dtype=1, w=256, k_idx=256, k_dtype=1, T=16, cap=1024, H_I=8,
                                 d_I=128, ctx_len=1000, q_pos0=1990, m=2, k=64, out_idx=256)
     need = L.csa2_prefill_topk_workspace_size(ctypes.byref(a))
-    assert need > 16 * 1000 * 4                      # approximate score rows of the chunk
+    assert need > 16 * 1000 * 8                      # candidate slots of the chunk
     assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 3
     assert "workspace" in _err()
     a.H_I = 4
@@ -113,3 +113,19 @@ def test_prefill_topk_argument_checks():
     assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 1
     a.ctx_len, a.T = 1000, 0
     assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 0    # nothing to do
+
+
+def test_pool_topk_argument_checks():
+    L = binding.lib()
+    f = L.csa2_pool_topk
+    # (block_max, rows, n_blocks, ld_bm, P_b, out_blocks, scores, ld, k, out_idx, stream)
+    assert f(None, 0, 100, 100, 64, None, None, 800, 32, None, None) == 0        # no rows: nothing to do
+    assert f(None, 2, 100, 100, 64, None, None, 800, 32, None, None) == 1        # null pointers
+    assert "null" in _err()
+    assert f(256, 2, 100, 100, 64, 256, 256, 800, 65, 256, None) == 1            # k > P_b
+    assert "k <= P_b" in _err()
+    assert f(256, 2, 100, 50, 64, 256, 256, 800, 32, 256, None) == 1             # ld_bm < n_blocks
+    assert f(256, 2, 100, 100, 4096, 256, 256, 800, 32, 256, None) == 2          # pool above 2,048 blocks
+    assert "csa2_topk_from_pool" in _err()
+    assert f(256, 2, 40000, 40000, 64, 256, 256, 800, 32, 256, None) == 2        # pool through super-blocks
+    assert f(256, 2, 32768, 32768, 64, 256, 256, 800, 32, 256, None) != 2        # largest direct pool

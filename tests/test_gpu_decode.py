@@ -1,0 +1,88 @@
+"""The decode composition (compressed_sparse_attention_05_amd.decode) against
+the oracle: one token for two sequences through a Full, a Reindex and a
+Reuse layer over one shared cache, with the token's own entry written first.
+Pool and index lists bit-exact; each layer's attention within 2e-3."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import csa2_inputs as ci
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.fail("gpu tests need a GPU")
+    import compressed_sparse_attention_05_amd as K
+    K.lib()
+    return K
+
+
+@pytest.mark.parametrize("k,P_b", [(256, 512), (600, 512)])
+def test_decode_step_full_reindex_reuse(K, k, P_b):
+    # k <= P_b: the Full layer's pool and top-k run as one launch;
+    # k > P_b: pool, then the Full top-k over the whole row
+    from compressed_sparse_attention_05_amd.decode import DecodeCache, DecodeStep, LayerInputs
+    dev = torch.device("cuda:0")
+    B, cap, D, H, d_I, H_I, W = 2, 20032, 512, 64, 128, 8, 128
+    ctx = [20000, 15001]
+    swa_len = [128, 50]
+    seed = 401
+    kv = ci.gaussian(seed, ci.TID_KV, (B, cap, D), clip=ci.NORM_BOUND)
+    kidx = ci.gaussian(seed, ci.TID_K_IDX, (B, cap, d_I), dtype=torch.bfloat16)
+    codes = torch.zeros((B, cap, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((B, cap, D // 16), dtype=torch.uint8, device=dev)
+    # every entry but the token's own (written by the step)
+    rows = torch.cat([torch.arange(b * cap, b * cap + ctx[b] - 1) for b in range(B)]).to(dev)
+    flat_kv = kv.reshape(B * cap, D).to(dev)
+    K.mxfp4_kv_write(flat_kv[rows], rows, codes, scales)
+    kc_rows = kidx.clone()
+    for b in range(B):
+        kc_rows[b, ctx[b] - 1:] = 0
+    kcache = K.tile_indexer_cache(kc_rows.to(dev))
+    new_rows = torch.tensor([b * cap + ctx[b] - 1 for b in range(B)], dtype=torch.int64)
+    cache = DecodeCache(codes=codes, scales=scales, k_idx=kcache,
+                        ctx_len=torch.tensor(ctx, dtype=torch.int32, device=dev),
+                        swa_len=torch.tensor(swa_len, dtype=torch.int32, device=dev))
+    layers = []
+    for li in range(3):
+        q = ci.gaussian(seed + li, ci.TID_Q, (B, H, D), dtype=torch.bfloat16)
+        swa = ci.gaussian(seed + li, ci.TID_SWA, (B, W, D), dtype=torch.bfloat16)
+        qi = ci.gaussian(seed + li, ci.TID_Q_IDX, (B, 1, H_I, d_I), dtype=torch.bfloat16)
+        wi = ci.uniform(seed + li, ci.TID_W, (B, 1, H_I))
+        layers.append((q, swa, qi, wi))
+    lin = [LayerInputs(q=q.to(dev), swa=swa.to(dev), q_idx=qi.to(dev), w=wi.to(dev)) for q, swa, qi, wi in layers]
+    step = DecodeStep("FXR", cache, lin, k=k, P_b=P_b,
+                      new_kv=flat_kv[new_rows.to(dev)].contiguous(),
+                      new_kidx=kidx.reshape(B * cap, d_I)[new_rows].contiguous().to(dev),
+                      dst_row=new_rows.to(dev))
+    step.run()
+    torch.cuda.synchronize()
+    sm = 1.0 / math.sqrt(D)
+    pool = step.pool.cpu().numpy()
+    idx_f = step.idx_bufs[0].cpu().numpy()
+    idx_x = step.idx_bufs[1].cpu().numpy()
+    for b in range(B):
+        oc, osc = oracle.mxfp4_encode(kv[b, :ctx[b]])
+        q0, s0, qi0, wi0 = layers[0]
+        sc = oracle.full_scores(qi0[b, 0], wi0[b, 0], kidx[b], ctx[b], cap)
+        opool = oracle.candidate_pool(oracle.block_max(sc, ctx[b], (cap + 7) // 8), P_b)
+        assert np.array_equal(pool[b, 0], opool), b
+        of = oracle.topk(sc, k)
+        assert np.array_equal(idx_f[b, 0], of), b
+        q1, s1, qi1, wi1 = layers[1]
+        ps = oracle.pool_scores(qi1[b, 0], wi1[b, 0], kidx[b], ctx[b], opool)
+        ox = oracle.pool_topk(ps, opool, k)
+        assert np.array_equal(idx_x[b, 0], ox), b
+        for li, oidx in ((0, of), (1, ox), (2, ox)):
+            q, swa = layers[li][0], layers[li][1]
+            want = oracle.attn_decode(q[b], oc, osc, oidx, swa[b], swa_len[b], sm)
+            err = float(np.max(np.abs(step.outs[li][b].cpu().numpy() - want)))
+            assert err < ATOL, (b, li, err)

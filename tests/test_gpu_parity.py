@@ -251,6 +251,28 @@ def test_pool_through_superblocks(K):
         assert np.array_equal(got[r], oracle.candidate_pool(bm[r], P_b)), r
 
 
+@pytest.mark.parametrize("n", [70000, 262144])
+def test_pool_topk_fused_equals_two_calls(K, n):
+    # csa2_pool_topk = pool then the Full top-k inside it, in one launch:
+    # 70,000 positions (16 block maxima per thread) and 262,144 (32 per
+    # thread, the largest row the fused path takes)
+    rng = np.random.default_rng(12)
+    rows, P_b = 4, 2048
+    v = np.abs(rng.standard_normal((rows, n))).astype(np.float32) * 10
+    v[1] = np.round(v[1])                       # ties everywhere
+    v[2, n - 9999:] = -np.inf                   # invisible tail
+    v[3, :] = -np.inf; v[3, 5:900:7] = 2.0      # fewer visible blocks than the pool
+    vis = [n, n, n - 9999, n]
+    nb = (n + 7) // 8
+    bm = np.stack([oracle.block_max(v[r], vis[r], nb) for r in range(rows)])
+    for k in (1, 64, 2048):
+        pool, idx = K.csa2_pool_topk(dev(torch.from_numpy(bm)), dev(torch.from_numpy(v)), P_b, k)
+        pool, idx = pool.cpu().numpy(), idx.cpu().numpy()
+        for r in range(rows):
+            assert np.array_equal(pool[r], oracle.candidate_pool(bm[r], P_b)), (r, k)
+            assert np.array_equal(idx[r], oracle.topk(v[r], k)), (r, k)
+
+
 def test_topk_small_rows_exhaustive(K):
     rng = np.random.default_rng(8)
     rows = rng.integers(0, 3, (500, 9)).astype(np.float32)
