@@ -161,6 +161,21 @@ class DecodeStep:
                                (ctypes.byref(aa), bd._ptr(ws), nws, None)))
             self.layer_idx = cur_idx
 
+    def capture(self):
+        """Record one step into a HIP graph (torch.cuda.CUDAGraph) and return
+        it; graph.replay() then enqueues the whole step with one launch.  The
+        step allocates nothing and uses no memset, so every replay repeats
+        exactly the recorded kernels on the pre-bound buffers."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()                      # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            self.run()
+        return graph
+
     def run(self, stream=None, events=None):
         """Enqueue the whole step on `stream` (default: torch's current).
         events: optional dict name -> (start_event, end_event) to bracket calls."""
