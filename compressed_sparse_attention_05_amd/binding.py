@@ -51,6 +51,12 @@ class PrefillTopkArgs(ctypes.Structure):
                 ("q_pos0", i64), ("m", i32), ("k", i32), ("out_idx", P)]
 
 
+class DecodeSelectArgs(ctypes.Structure):
+    _fields_ = [("q_idx", P), ("q_dtype", i32), ("w", P), ("k_idx", P), ("k_dtype", i32),
+                ("ctx_len", P), ("B", i64), ("cap", i64), ("H_I", i32), ("d_I", i32),
+                ("P_b", i32), ("k", i32), ("out_pool", P), ("out_idx", P)]
+
+
 SIGNATURES = {
     "csa2_version": (ctypes.c_char_p, []),
     "csa2_last_error": (ctypes.c_char_p, []),
@@ -63,6 +69,9 @@ SIGNATURES = {
     "csa2_build_candidate_pool": (ctypes.c_int, [P, i64, i64, i64, i32, P, P, ctypes.c_size_t, P]),
     "csa2_topk_from_pool": (ctypes.c_int, [P, i64, i64, P, i32, i32, P, P]),
     "csa2_pool_topk": (ctypes.c_int, [P, i64, i64, i64, i32, P, P, i64, i32, P, P]),
+    "csa2_decode_select_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(DecodeSelectArgs)]),
+    "csa2_decode_scan": (ctypes.c_int, [ctypes.POINTER(DecodeSelectArgs), P, ctypes.c_size_t, P]),
+    "csa2_decode_select": (ctypes.c_int, [ctypes.POINTER(DecodeSelectArgs), P, ctypes.c_size_t, P]),
     "csa2_sparse_attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), P, ctypes.c_size_t, P]),
     "csa2_sparse_attn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnPrefillArgs)]),
@@ -333,6 +342,35 @@ def csa2_sparse_attn_prefill(q, codes, scales, idx, swa, W: int, q_pos0: int, *,
     _check(L.csa2_sparse_attn_prefill(ctypes.byref(a), _ptr(ws), 0 if ws is None else ws.numel(),
                                       _stream(stream)))
     return out
+
+
+def csa2_decode_select(q_idx, w, k_idx, ctx_len, P_b: int, k: int, *, out_pool=None, out=None,
+                       workspace=None, stream=None):
+    """Decode Full layer: candidate pool [B][P_b] and top-k [B][k] from the
+    indexer query q_idx [B][8][128] bf16 (or [B][1][8][128]), w [B][8] f32,
+    the tiled indexer cache k_idx [B][cap][128] bf16 and ctx_len [B] int32,
+    with the matrix-core scan (csa2_decode_scan then csa2_decode_select).
+    Equals csa2_index_score + csa2_build_candidate_pool + csa2_topk_from_pool."""
+    for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx"), (ctx_len, "ctx_len")):
+        _dev(t, nm)
+    B, cap, d_I = k_idx.shape
+    H_I = q_idx.shape[-2]
+    if out_pool is None:
+        out_pool = torch.empty((B, P_b), dtype=torch.int32, device=q_idx.device)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
+    a = DecodeSelectArgs(q_idx=q_idx.data_ptr(), q_dtype=_dtype(q_idx, "q_idx"), w=w.data_ptr(),
+                         k_idx=k_idx.data_ptr(), k_dtype=_dtype(k_idx, "k_idx"), ctx_len=ctx_len.data_ptr(),
+                         B=B, cap=cap, H_I=H_I, d_I=d_I, P_b=int(P_b), k=int(k), out_pool=out_pool.data_ptr(),
+                         out_idx=out.data_ptr())
+    L = lib()
+    need = L.csa2_decode_select_workspace_size(ctypes.byref(a))
+    ws = workspace if workspace is not None else _workspace(need, q_idx.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _stream(stream)
+    _check(L.csa2_decode_scan(ctypes.byref(a), _ptr(ws), nbytes, st))
+    _check(L.csa2_decode_select(ctypes.byref(a), _ptr(ws), nbytes, st))
+    return out_pool, out
 
 
 def csa2_prefill_topk(q_idx, w, k_idx, ctx_len: int, q_pos0: int, m: int, k: int, *, out=None,

@@ -306,9 +306,61 @@ int check_prefill_topk(const csa2_prefill_topk_args* a) {
         return fail(CSA2_E_INVALID, "%s: q_idx and k_idx must be 16-byte aligned", fn);
     return CSA2_OK;
 }
+
+int check_decode_select(const csa2_decode_select_args* a) {
+    const char* fn = "csa2_decode_select";
+    if (!a) return fail(CSA2_E_INVALID, "%s: args is null", fn);
+    if (a->B < 0) return fail(CSA2_E_INVALID, "%s: B < 0", fn);
+    if (a->cap <= 0 || a->cap % 64 != 0)
+        return fail(CSA2_E_INVALID, "%s: cap=%lld must be a positive multiple of 64", fn,
+                    static_cast<long long>(a->cap));
+    if (a->k < 1 || a->P_b < 1 || a->k > a->P_b)
+        return fail(CSA2_E_INVALID, "%s: need 1 <= k <= P_b (the pool holds the top-k only then)", fn);
+    if (!valid_dtype(a->q_dtype) || !valid_dtype(a->k_dtype)) return fail(CSA2_E_INVALID, "%s: bad dtype", fn);
+    if (a->q_dtype != CSA2_BF16 || a->k_dtype != CSA2_BF16)
+        return fail(CSA2_E_UNSUPPORTED, "%s: q and k must be bf16", fn);
+    if (!csa2::decode_select_supported(a->cap, a->H_I, a->d_I, a->P_b, a->k))
+        return fail(CSA2_E_UNSUPPORTED,
+                    "%s: H_I=%d d_I=%d cap=%lld P_b=%d outside the one-workgroup path (8 x 128, cap <= 262,144, "
+                    "P_b <= 2048): use csa2_index_score with the pool and top-k calls",
+                    fn, a->H_I, a->d_I, static_cast<long long>(a->cap), a->P_b);
+    if (a->B > 0 && (!a->q_idx || !a->w || !a->k_idx || !a->ctx_len || !a->out_pool || !a->out_idx))
+        return fail(CSA2_E_INVALID, "%s: null tensor", fn);
+    if (!aligned(a->q_idx, 16) || !aligned(a->k_idx, 16))
+        return fail(CSA2_E_INVALID, "%s: q_idx and k_idx must be 16-byte aligned", fn);
+    return CSA2_OK;
+}
 }  // namespace
 
 extern "C" {
+
+size_t csa2_decode_select_workspace_size(const csa2_decode_select_args* a) {
+    if (check_decode_select(a) != CSA2_OK) return 0;
+    return csa2::decode_select_workspace_bytes(a->B, a->cap);
+}
+
+static int decode_select_call(const csa2_decode_select_args* a, void* ws, size_t ws_bytes, void* stream, bool scan) {
+    const char* fn = scan ? "csa2_decode_scan" : "csa2_decode_select";
+    const int rc = check_decode_select(a);
+    if (rc != CSA2_OK) return rc;
+    if (a->B == 0) return ok();
+    const size_t need = csa2::decode_select_workspace_bytes(a->B, a->cap);
+    if (!ws || ws_bytes < need) return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(CSA2_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    csa2::DecodeSelectLaunch L;
+    L.q_idx = a->q_idx; L.w = a->w; L.k_idx = a->k_idx; L.ctx_len = a->ctx_len; L.B = a->B; L.cap = a->cap;
+    L.P_b = a->P_b; L.k = a->k; L.out_pool = a->out_pool; L.out_idx = a->out_idx;
+    return device_status(scan ? csa2::launch_decode_scan(L, ws, as_stream(stream))
+                              : csa2::launch_decode_select(L, ws, as_stream(stream)), fn);
+}
+
+int csa2_decode_scan(const csa2_decode_select_args* a, void* ws, size_t ws_bytes, void* stream) {
+    return decode_select_call(a, ws, ws_bytes, stream, true);
+}
+
+int csa2_decode_select(const csa2_decode_select_args* a, void* ws, size_t ws_bytes, void* stream) {
+    return decode_select_call(a, ws, ws_bytes, stream, false);
+}
 
 size_t csa2_prefill_topk_workspace_size(const csa2_prefill_topk_args* a) {
     if (check_prefill_topk(a) != CSA2_OK) return 0;

@@ -80,4 +80,19 @@ size_t prefill_topk_workspace_bytes(int64_t T, int32_t ctx_len, int64_t q_pos0, 
 int prefill_topk_max_k();
 hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st);
 
+struct DecodeSelectLaunch {
+    const void* q_idx;      // [B][8][128] bf16
+    const float* w;         // [B][8]
+    const void* k_idx;      // tiled bf16 indexer cache, [B][cap]
+    const int32_t* ctx_len; // [B] (device)
+    int64_t B, cap;
+    int32_t P_b, k;
+    int32_t* out_pool;      // [B][P_b]
+    int32_t* out_idx;       // [B][k]
+};
+bool decode_select_supported(int64_t cap, int H_I, int d_I, int P_b, int k);
+size_t decode_select_workspace_bytes(int64_t B, int64_t cap);
+hipError_t launch_decode_scan(const DecodeSelectLaunch& L, void* ws, hipStream_t st);
+hipError_t launch_decode_select(const DecodeSelectLaunch& L, void* ws, hipStream_t st);
+
 }  // namespace csa2

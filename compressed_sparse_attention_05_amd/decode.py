@@ -51,13 +51,21 @@ class DecodeStep:
     build_pool is set (X layers need a pool: built here or passed in).
     new_kv / new_kidx / dst_row: the token's main-KV row and indexer-K row,
     written first (mxfp4_kv_write) so the new entry is visible to scoring.
+    mfma_select: the Full layer that builds the pool scores on the matrix
+    cores and selects with exact rescoring near the thresholds
+    (csa2_decode_scan + csa2_decode_select) where that path applies (8 x 128
+    bf16 indexer, cap <= 262,144, k <= P_b <= 2048); the results are the same
+    as the exact scan's.  Off by default: on MI355X at 128K x 8 rows its scan
+    is only 3 us faster than the exact one, while its one-workgroup-per-row
+    selection (band rescoring) takes about 73 us against 26 us for the fused
+    pool/top-k.
     """
 
     def __init__(self, schedule: str, cache: DecodeCache, layers: List[LayerInputs], *, k: int,
                  P_b: int = 2048, new_kv: Optional[torch.Tensor] = None,
                  new_kidx: Optional[torch.Tensor] = None, dst_row: Optional[torch.Tensor] = None,
                  pool: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
-                 build_pool: bool = True):
+                 build_pool: bool = True, mfma_select: bool = False):
         assert len(schedule) == len(layers)
         self.schedule, self.cache, self.layers, self.k, self.P_b = schedule, cache, layers, k, P_b
         B, cap, half = cache.codes.shape
@@ -95,6 +103,24 @@ class DecodeStep:
                 if use_pool and not pool_built:
                     raise ValueError("a Reindex layer needs a pool from an earlier Full layer")
                 want_bm = mode == "F" and build_pool and not pool_built
+                if (want_bm and mfma_select and lay.q_idx.dtype == torch.bfloat16
+                        and cache.k_idx.dtype == torch.bfloat16 and lay.q_idx.shape[-2:] == (8, 128)
+                        and cap % 64 == 0 and cap <= 262144 and k <= P_b <= 2048):
+                    da = bd.DecodeSelectArgs(
+                        q_idx=lay.q_idx.data_ptr(), q_dtype=bd.CSA2_BF16, w=lay.w.data_ptr(),
+                        k_idx=cache.k_idx.data_ptr(), k_dtype=bd.CSA2_BF16, ctx_len=cache.ctx_len.data_ptr(),
+                        B=B, cap=cap, H_I=8, d_I=128, P_b=P_b, k=k, out_pool=self.pool.data_ptr(),
+                        out_idx=idx.data_ptr())
+                    dn = self.L.csa2_decode_select_workspace_size(ctypes.byref(da))
+                    dws = torch.empty(max(dn, 256), dtype=torch.uint8, device=dev)
+                    self._keep += [da, dws]
+                    self.calls.append((f"score{li}", self.L.csa2_decode_scan, (ctypes.byref(da), bd._ptr(dws), dn, None)))
+                    self.calls.append((f"pool{li}", self.L.csa2_decode_select,
+                                       (ctypes.byref(da), bd._ptr(dws), dn, None)))
+                    pool_built = True
+                    cur_idx = idx
+                    self._attn(li, lay, cur_idx)
+                    continue
                 sa = bd.ScoreArgs(
                     q_idx=lay.q_idx.data_ptr(), q_dtype=bd._dtype(lay.q_idx, "q_idx"), w=lay.w.data_ptr(),
                     k_idx=cache.k_idx.data_ptr(), k_dtype=bd._dtype(cache.k_idx, "k_idx"), B=B, Tq=1,
@@ -149,17 +175,21 @@ class DecodeStep:
                     raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
             else:
                 raise ValueError(f"unknown layer mode {mode!r}")
-            aa = bd.AttnArgs(q=lay.q.data_ptr(), q_dtype=bd._dtype(lay.q, "q"), codes=cache.codes.data_ptr(),
-                             scales=cache.scales.data_ptr(), cap=cap, idx=cur_idx.data_ptr(), k=k,
-                             swa=lay.swa.data_ptr(), swa_dtype=bd._dtype(lay.swa, "swa"), W=lay.swa.shape[1],
-                             swa_len=cache.swa_len.data_ptr(), B=B, H=lay.q.shape[1], D=D,
-                             sm_scale=self.sm_scale, out=self.outs[li].data_ptr())
-            nws = self.L.csa2_sparse_attn_decode_workspace_size(ctypes.byref(aa))
-            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
-            self._keep += [aa, ws]
-            self.calls.append((f"attn{li}", self.L.csa2_sparse_attn_decode,
-                               (ctypes.byref(aa), bd._ptr(ws), nws, None)))
-            self.layer_idx = cur_idx
+            self._attn(li, lay, cur_idx)
+
+    def _attn(self, li: int, lay: "LayerInputs", cur_idx: torch.Tensor) -> None:
+        cache, B, cap, D, k = self.cache, self.B, self.cap, self.D, self.k
+        aa = bd.AttnArgs(q=lay.q.data_ptr(), q_dtype=bd._dtype(lay.q, "q"), codes=cache.codes.data_ptr(),
+                         scales=cache.scales.data_ptr(), cap=cap, idx=cur_idx.data_ptr(), k=k,
+                         swa=lay.swa.data_ptr(), swa_dtype=bd._dtype(lay.swa, "swa"), W=lay.swa.shape[1],
+                         swa_len=cache.swa_len.data_ptr(), B=B, H=lay.q.shape[1], D=D,
+                         sm_scale=self.sm_scale, out=self.outs[li].data_ptr())
+        nws = self.L.csa2_sparse_attn_decode_workspace_size(ctypes.byref(aa))
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=cache.codes.device)
+        self._keep += [aa, ws]
+        self.calls.append((f"attn{li}", self.L.csa2_sparse_attn_decode,
+                           (ctypes.byref(aa), bd._ptr(ws), nws, None)))
+        self.layer_idx = cur_idx
 
     def capture(self):
         """Record one step into a HIP graph (torch.cuda.CUDAGraph) and return

@@ -296,6 +296,48 @@ typedef struct csa2_prefill_topk_args {
 size_t csa2_prefill_topk_workspace_size(const csa2_prefill_topk_args *a);
 int csa2_prefill_topk(const csa2_prefill_topk_args *a, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * csa2_decode_scan, csa2_decode_select - the decode Full layer's candidate
+ * pool and top-k ([KVC] sections 2-3) from the indexer query, with the
+ * products on the matrix cores.  csa2_decode_scan computes the approximate
+ * scores, their block maxima and each row's largest key norm into the
+ * workspace; csa2_decode_select, called next with the same arguments and
+ * workspace (on the same stream, or after it), selects.  Together: the same
+ * outputs, bit for bit, as csa2_index_score (Tq = 1, with block maxima)
+ * followed by csa2_build_candidate_pool and csa2_topk_from_pool: the
+ * approximate scores carry a proven error bound (from ||q_h||, |w_h| and
+ * the row's largest key norm), and the keys and
+ * blocks whose approximate value lies within that bound of a threshold are
+ * rescored with the exact float32 chains.  A row whose band of such keys
+ * outgrows the fixed on-chip budget is redone from exact scores (same
+ * result, slower).
+ *   q_idx [B][H_I][d_I] bf16, w [B][H_I] f32   (H_I = 8, d_I = 128 only)
+ *   k_idx [B][cap] tiled indexer cache (csa2_index_score), bf16,
+ *         cap % 64 == 0, cap <= 262,144
+ *   ctx_len [B] int32 (device): visible entries per sequence
+ *   out_pool [B][P_b] ascending block ids, -1 padded (P_b <= 2048)
+ *   out_idx [B][k] ascending positions, -1 padded (1 <= k <= P_b)
+ * Workspace: csa2_decode_select_workspace_size (4 B per cache entry, plus
+ * block maxima and one key-norm maximum per 256 entries); 256-byte aligned.
+ * Errors: CSA2_E_INVALID (bad arguments), CSA2_E_UNSUPPORTED (shape outside
+ * this path), CSA2_E_WORKSPACE (short workspace); nothing is launched then.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_decode_select_args {
+    const void *q_idx;  int32_t q_dtype;  /* [B][H_I][d_I] */
+    const float *w;                       /* [B][H_I] */
+    const void *k_idx;  int32_t k_dtype;  /* [B][cap] tiled */
+    const int32_t *ctx_len;               /* [B] */
+    int64_t B, cap;
+    int32_t H_I, d_I;
+    int32_t P_b, k;
+    int32_t *out_pool;                    /* [B][P_b] */
+    int32_t *out_idx;                     /* [B][k] */
+} csa2_decode_select_args;
+
+size_t csa2_decode_select_workspace_size(const csa2_decode_select_args *a);
+int csa2_decode_scan(const csa2_decode_select_args *a, void *ws, size_t ws_bytes, void *stream);
+int csa2_decode_select(const csa2_decode_select_args *a, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

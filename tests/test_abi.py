@@ -129,3 +129,26 @@ def test_pool_topk_argument_checks():
     assert "csa2_topk_from_pool" in _err()
     assert f(256, 2, 40000, 40000, 64, 256, 256, 800, 32, 256, None) == 2        # pool through super-blocks
     assert f(256, 2, 32768, 32768, 64, 256, 256, 800, 32, 256, None) != 2        # largest direct pool
+
+
+def test_decode_select_argument_checks():
+    L = binding.lib()
+    a = binding.DecodeSelectArgs(q_idx=256, q_dtype=1, w=256, k_idx=256, k_dtype=1, ctx_len=256, B=4, cap=4096,
+                                 H_I=8, d_I=128, P_b=64, k=32, out_pool=256, out_idx=256)
+    need = L.csa2_decode_select_workspace_size(ctypes.byref(a))
+    assert need >= 4 * 4096 * 4                       # approximate scores of every cache entry
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 3
+    assert "workspace" in _err()
+    assert L.csa2_decode_select(ctypes.byref(a), None, 0, None) == 3
+    a.k = 65                                          # k > P_b: the pool would not hold the top-k
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 1
+    a.k, a.H_I = 32, 4
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 2
+    a.H_I, a.cap = 8, 262208                          # beyond the one-workgroup selection
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 2
+    a.cap, a.q_dtype = 4000, 1                        # not a multiple of 64
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 1
+    a.cap, a.q_dtype = 4096, 0
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 2
+    a.q_dtype, a.B = 1, 0
+    assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 0  # nothing to do

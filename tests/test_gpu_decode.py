@@ -25,9 +25,10 @@ def K():
     return K
 
 
-@pytest.mark.parametrize("k,P_b", [(256, 512), (600, 512)])
-def test_decode_step_full_reindex_reuse(K, k, P_b):
-    # k <= P_b: the Full layer's pool and top-k run as one launch;
+@pytest.mark.parametrize("k,P_b,mfma", [(256, 512, False), (600, 512, False), (256, 512, True)])
+def test_decode_step_full_reindex_reuse(K, k, P_b, mfma):
+    # k <= P_b: the Full layer's pool and top-k run as one launch (or, with
+    # mfma, the matrix-core scan and the band-exact selection);
     # k > P_b: pool, then the Full top-k over the whole row
     from compressed_sparse_attention_05_amd.decode import DecodeCache, DecodeStep, LayerInputs
     dev = torch.device("cuda:0")
@@ -62,7 +63,7 @@ def test_decode_step_full_reindex_reuse(K, k, P_b):
     step = DecodeStep("FXR", cache, lin, k=k, P_b=P_b,
                       new_kv=flat_kv[new_rows.to(dev)].contiguous(),
                       new_kidx=kidx.reshape(B * cap, d_I)[new_rows].contiguous().to(dev),
-                      dst_row=new_rows.to(dev))
+                      dst_row=new_rows.to(dev), mfma_select=mfma)
     step.run()
     torch.cuda.synchronize()
     sm = 1.0 / math.sqrt(D)
