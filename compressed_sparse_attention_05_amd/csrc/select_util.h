@@ -200,21 +200,30 @@ __device__ uint32_t count_valid(Get get, int64_t n, uint32_t* wave_tot) {
 //     sign and most exponent bits, which a fixed top digit would spend a pass
 //     on).  Two passes usually resolve the k-th key.
 //  2. Each pass counts the keys that still match the resolved prefix into an
-//     LDS histogram; a workgroup scan over the bins from the top finds the
-//     digit holding the k-th key.
-//  3. Emission: two workgroup scans give each thread its tie rank and output
-//     offset, and it writes its chosen slots in order, so ties go to the
+//     LDS histogram.  Thread t owns bins kSelBins-8-8t .. kSelBins-1-8t, so
+//     thread order is descending bin order.  Every wave then finds the digit
+//     holding the k-th key on its own (the wave totals locate the owning
+//     wave, whose bins it rereads), so no result is published through LDS.
+//     Two histograms alternate: a thread clears its bins of the other one
+//     after the pass's first barrier, when every wave has finished reading
+//     them, so a pass has two barriers.
+//  3. Emission: one workgroup scan of (keys above T, keys equal to T) packed
+//     into 16-bit halves gives each thread its output offset and its share
+//     of the ties; it writes its chosen slots in order, so ties go to the
 //     lowest slots and the output is sorted without a sort.
 constexpr int kSelMax = 32768;
 constexpr int kSelBits = 13;
 constexpr int kSelBins = 1 << kSelBits;          // 8 bins per thread
 static_assert(kSelBins == 8 * kThreads, "bin ownership assumes 8 bins per thread");
+static_assert(kSelMax < 65536, "emission packs two counts into 16-bit halves");
 
 struct alignas(16) SelLds {
-    uint32_t hist[kSelBins];
+    uint32_t hist[2][kSelBins];
     uint32_t wave_tot[kWaves];
     uint32_t wave_min[kWaves];
     uint32_t wave_max[kWaves];
+    uint32_t pass_tot[2][kWaves];
+    uint32_t emit_tot[kWaves];
     uint32_t res[4];
 };
 
@@ -242,14 +251,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_t
     return before + incl - v;
 }
 
-// Choose the k best keys of the workgroup's slots (thread t: slots
-// [tR, tR + R) in kk, 0 = empty) and call out(rank, j) for each chosen slot
-// tR + j in ascending slot order.  Returns min(k, #nonempty).
-template <int R, class Out>
-__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out) {
+// Stage 1: nonempty count, smallest and largest nonempty key of the
+// workgroup; also clears this thread's bins of hist[0] for the first pass.
+// One barrier; wave_tot/min/max are read only here.
+template <int R>
+__device__ __forceinline__ uint32_t sel_stats(const uint32_t (&kk)[R], SelLds& sh, uint32_t& mn_out, uint32_t& mx_out) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-
-    // ---- 1. count, smallest and largest nonempty key
     uint32_t cnt = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -265,6 +272,11 @@ __device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, 
         mx = omx > mx ? omx : mx;
     }
     if (lane == 0) { sh.wave_tot[wv] = cnt; sh.wave_min[wv] = mn; sh.wave_max[wv] = mx; }
+    {
+        const int hb = kSelBins - 8 - 8 * tid;
+        *reinterpret_cast<uint4*>(&sh.hist[0][hb]) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sh.hist[0][hb + 4]) = make_uint4(0u, 0u, 0u, 0u);
+    }
     __syncthreads();
     uint32_t n_valid = 0;
     mn = 0xffffffffu; mx = 0u;
@@ -274,72 +286,135 @@ __device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, 
         mn = sh.wave_min[w] < mn ? sh.wave_min[w] : mn;
         mx = sh.wave_max[w] > mx ? sh.wave_max[w] : mx;
     }
-    __syncthreads();
+    mn_out = mn; mx_out = mx;
+    return n_valid;
+}
+
+// Stage 2: the exact need-th largest key T (need >= 1 nonempty keys exist)
+// and, on return, need = how many keys equal to T belong to the selection.
+// hist[0] must be clear (sel_stats); both histograms are left dirty.
+template <int R>
+__device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t mn, uint32_t mx, uint32_t& need,
+                                               SelLds& sh) {
+    if (mn == mx) return mn;                       // every nonempty key is T
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int hb = kSelBins - 8 - 8 * tid;         // this thread's bins
+    int top = 31 - __builtin_clz(mn ^ mx);         // highest bit not shared
+    uint64_t known = static_cast<uint64_t>(mn) >> (top + 1);
+    int buf = 0;
+    while (top >= 0) {
+        const int nb = top + 1 < kSelBits ? top + 1 : kSelBits;
+        const int shift = top + 1 - nb;
+        const uint32_t dmask = (1u << nb) - 1u;
+        // keys match the resolved prefix when their bits above `top` equal
+        // it (all keys do before the first pass below bit 31)
+        const bool match_all = top == 31;
+        const int pshift = match_all ? 0 : top + 1;
+        const uint32_t known32 = static_cast<uint32_t>(known);
+        uint32_t* hist = sh.hist[buf];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const bool ok = kk[j] != 0u && (match_all || (kk[j] >> pshift) == known32);
+            if (ok) atomicAdd(&hist[(kk[j] >> shift) & dmask], 1u);
+            if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        // the other histogram was last read before this barrier: clear this
+        // thread's bins of it for the next pass
+        *reinterpret_cast<uint4*>(&sh.hist[buf ^ 1][hb]) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sh.hist[buf ^ 1][hb + 4]) = make_uint4(0u, 0u, 0u, 0u);
+        {
+            const uint4 lo = *reinterpret_cast<const uint4*>(&hist[hb]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(&hist[hb + 4]);
+            uint32_t sum = lo.x + lo.y + lo.z + lo.w + hi.x + hi.y + hi.z + hi.w;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            if (lane == 0) sh.pass_tot[buf][wv] = sum;
+        }
+        __syncthreads();
+        // the wave holding the need-th key (waves in descending bin order)
+        uint32_t acc = 0;
+        int W = kWaves - 1;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t t = sh.pass_tot[buf][w];
+            if (W == kWaves - 1 && w < kWaves - 1) {
+                if (acc + t >= need) W = w; else acc += t;
+            }
+        }
+        W = __builtin_amdgcn_readfirstlane(W);
+        acc = __builtin_amdgcn_readfirstlane(acc);
+        // lane l rereads the bins of thread 64W + l
+        const int hbw = kSelBins - 8 - 8 * (64 * W + lane);
+        const uint4 lo = *reinterpret_cast<const uint4*>(&hist[hbw]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&hist[hbw + 4]);
+        const uint32_t c[8] = {hi.w, hi.z, hi.y, hi.x, lo.w, lo.z, lo.y, lo.x};
+        uint32_t s8 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s8 += c[i];
+        uint32_t incl = s8;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        const uint32_t excl = acc + incl - s8;
+        const bool mine = excl < need && excl + s8 >= need;
+        uint32_t digit = 0, above = 0;
+        if (mine) {
+            uint32_t a = excl;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (a + c[i] >= need) { digit = static_cast<uint32_t>(hbw + 7 - i); above = a; break; }
+                a += c[i];
+            }
+        }
+        const uint64_t bal = __ballot(mine);
+        const int src = bal ? static_cast<int>(__builtin_ctzll(bal)) : 0;
+        digit = __shfl(digit, src);
+        above = __shfl(above, src);
+        known = (known << nb) | digit;
+        need -= above;
+        top = shift - 1;
+        buf ^= 1;
+    }
+    return static_cast<uint32_t>(known);
+}
+
+// Choose the k best keys of the workgroup's slots (thread t: slots
+// [tR, tR + R) in kk, 0 = empty) and call out(rank, j) for each chosen slot
+// tR + j in ascending slot order.  Returns min(k, #nonempty).
+template <int R, class Out>
+__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint32_t mn, mx;
+    const uint32_t n_valid = sel_stats<R>(kk, sh, mn, mx);
     const uint32_t k_eff = n_valid < k ? n_valid : k;
     if (k_eff == 0) return 0;
+    uint32_t need = k_eff;
+    const uint32_t T = sel_passes<R>(kk, mn, mx, need, sh);
 
-    // ---- 2. radix passes below the shared prefix
-    uint32_t need = k_eff, T;
-    if (mn == mx) {
-        T = mn;                                    // every nonempty key is T
-    } else {
-        int top = 31 - __builtin_clz(mn ^ mx);     // highest bit not shared
-        uint64_t known = static_cast<uint64_t>(mn) >> (top + 1);
-        while (top >= 0) {
-            const int nb = top + 1 < kSelBits ? top + 1 : kSelBits;
-            const int shift = top + 1 - nb;
-            const uint32_t dmask = (1u << nb) - 1u;
-            // keys match the resolved prefix when their bits above `top`
-            // equal it (all keys do before the first pass below bit 31)
-            const bool match_all = top == 31;
-            const int pshift = match_all ? 0 : top + 1;
-            const uint32_t known32 = static_cast<uint32_t>(known);
-            for (int i = tid; i < kSelBins; i += kThreads) sh.hist[i] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const bool ok = kk[j] != 0u && (match_all || (kk[j] >> pshift) == known32);
-                if (ok) atomicAdd(&sh.hist[(kk[j] >> shift) & dmask], 1u);
-                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-            }
-            __syncthreads();
-            // thread t holds bins kSelBins-1-8t down to kSelBins-8-8t, so
-            // thread order is descending bin order
-            const int hb = kSelBins - 8 - 8 * tid;
-            const uint4 lo = *reinterpret_cast<const uint4*>(&sh.hist[hb]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(&sh.hist[hb + 4]);
-            const uint32_t c[8] = {hi.w, hi.z, hi.y, hi.x, lo.w, lo.z, lo.y, lo.x};
-            uint32_t sum = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sum += c[i];
-            uint32_t tot;
-            const uint32_t excl = block_excl_scan(sum, sh.wave_tot, tot);
-            if (excl < need && excl + sum >= need) {
-                uint32_t acc = excl;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (acc + c[i] >= need) { sh.res[0] = hb + 7 - i; sh.res[1] = acc; break; }
-                    acc += c[i];
-                }
-            }
-            __syncthreads();
-            known = (known << nb) | sh.res[0];
-            need -= sh.res[1];
-            top = shift - 1;
-            __syncthreads();
-        }
-        T = static_cast<uint32_t>(known);
-    }
-
-    // ---- 3. ordered emission
+    // ---- 3. ordered emission: one scan of (above << 16 | ties)
     uint32_t above = 0, ties = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j) { above += kk[j] > T; ties += kk[j] == T; }
-    uint32_t tmp;
-    const uint32_t ties_before = block_excl_scan(ties, sh.wave_tot, tmp);
+    const uint32_t packed = (above << 16) | ties;
+    uint32_t incl = packed;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) sh.emit_tot[wv] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) before += (i < wv) ? sh.emit_tot[i] : 0u;
+    const uint32_t excl = before + incl - packed;
+    const uint32_t above_before = excl >> 16, ties_before = excl & 0xffffu;
     uint32_t take = need > ties_before ? need - ties_before : 0u;
     if (take > ties) take = ties;
-    uint32_t at = block_excl_scan(above + take, sh.wave_tot, tmp);
+    uint32_t at = above_before + (need < ties_before ? need : ties_before);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const bool tie_pick = kk[j] == T && take > 0;
@@ -359,83 +434,15 @@ __device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, 
 // select_run (stages 1 and 2 only).  Returns min(k, #nonempty).
 template <int R>
 __device__ uint32_t kth_key(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, uint32_t& T_out, uint32_t& need_out) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    uint32_t cnt = 0, mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        cnt += kk[j] != 0u;
-        mn = (kk[j] != 0u && kk[j] < mn) ? kk[j] : mn;
-        mx = kk[j] > mx ? kk[j] : mx;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        cnt += __shfl_xor(cnt, off);
-        const uint32_t omn = __shfl_xor(mn, off), omx = __shfl_xor(mx, off);
-        mn = omn < mn ? omn : mn;
-        mx = omx > mx ? omx : mx;
-    }
-    if (lane == 0) { sh.wave_tot[wv] = cnt; sh.wave_min[wv] = mn; sh.wave_max[wv] = mx; }
-    __syncthreads();
-    uint32_t n_valid = 0;
-    mn = 0xffffffffu; mx = 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        n_valid += sh.wave_tot[w];
-        mn = sh.wave_min[w] < mn ? sh.wave_min[w] : mn;
-        mx = sh.wave_max[w] > mx ? sh.wave_max[w] : mx;
-    }
-    __syncthreads();
+    uint32_t mn, mx;
+    const uint32_t n_valid = sel_stats<R>(kk, sh, mn, mx);
     const uint32_t k_eff = n_valid < k ? n_valid : k;
     T_out = 0u; need_out = 0u;
-    if (k_eff == 0) return 0;
-    uint32_t need = k_eff, T;
-    if (mn == mx) {
-        T = mn;
-    } else {
-        int top = 31 - __builtin_clz(mn ^ mx);
-        uint64_t known = static_cast<uint64_t>(mn) >> (top + 1);
-        while (top >= 0) {
-            const int nb = top + 1 < kSelBits ? top + 1 : kSelBits;
-            const int shift = top + 1 - nb;
-            const uint32_t dmask = (1u << nb) - 1u;
-            const bool match_all = top == 31;
-            const int pshift = match_all ? 0 : top + 1;
-            const uint32_t known32 = static_cast<uint32_t>(known);
-            for (int i = tid; i < kSelBins; i += kThreads) sh.hist[i] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const bool ok = kk[j] != 0u && (match_all || (kk[j] >> pshift) == known32);
-                if (ok) atomicAdd(&sh.hist[(kk[j] >> shift) & dmask], 1u);
-                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-            }
-            __syncthreads();
-            const int hb = kSelBins - 8 - 8 * tid;
-            const uint4 lo = *reinterpret_cast<const uint4*>(&sh.hist[hb]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(&sh.hist[hb + 4]);
-            const uint32_t c[8] = {hi.w, hi.z, hi.y, hi.x, lo.w, lo.z, lo.y, lo.x};
-            uint32_t sum = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sum += c[i];
-            uint32_t tot;
-            const uint32_t excl = block_excl_scan(sum, sh.wave_tot, tot);
-            if (excl < need && excl + sum >= need) {
-                uint32_t acc = excl;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (acc + c[i] >= need) { sh.res[0] = hb + 7 - i; sh.res[1] = acc; break; }
-                    acc += c[i];
-                }
-            }
-            __syncthreads();
-            known = (known << nb) | sh.res[0];
-            need -= sh.res[1];
-            top = shift - 1;
-            __syncthreads();
-        }
-        T = static_cast<uint32_t>(known);
-    }
-    T_out = T;
+    if (k_eff == 0) { __syncthreads(); return 0; }
+    uint32_t need = k_eff;
+    T_out = sel_passes<R>(kk, mn, mx, need, sh);
     need_out = need;
+    // callers reuse wave_tot (block_excl_scan) next
+    __syncthreads();
     return k_eff;
 }
