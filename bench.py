@@ -17,8 +17,10 @@ roofline and for "eager_ms_per_step".
 Prints ONE JSON line: queries/s for the workload, the dominant kernel's
 roofline (the Full-mode indexer scan, timed live with HIP events on the
 stream it runs on), the CPU oracle timed on a bounded sample, and under
-"secondary" the two 1M-context decode workloads (decoder block 2 with its
-Reindex layer, and the full 20-layer step at B=64).
+"secondary" the 1M-context decode workloads (decoder block 2 with its
+Reindex layer, the decoder's 20-layer step at B=64, and the 38-layer step
+that adds the encoder's three Full + 5 Reuse blocks at m = 2) and the
+prefill chunk.
 """
 from __future__ import annotations
 
@@ -85,12 +87,35 @@ class InputSet:
         self.new_kv = ci.gaussian_rows(seed, ci.TID_KV, self.dst_row, D, dtype=torch.bfloat16,
                                        clip=ci.NORM_BOUND)
         self.new_kidx = ci.gaussian_rows(seed, ci.TID_K_IDX, self.dst_row, d_I, dtype=torch.bfloat16)
+        # encoder KV sets (one per E layer): N / enc_m complete entries; the
+        # step's token (position N-1) completes the last one and writes it
+        self.enc_caches, self.enc_writes = [], []
+        self.enc_q_pos = torch.full((B,), N - 1, dtype=torch.int64, device=dev)
+        for e in range(w.schedule.count("E")):
+            seed_e = seed + 7919 * (e + 1)
+            cap_e = N // w.enc_m
+            codes_e = torch.empty((B, cap_e, D // 2), dtype=torch.uint8, device=dev)
+            scales_e = torch.empty((B, cap_e, D // 16), dtype=torch.uint8, device=dev)
+            fill_kv_cache(K, codes_e, scales_e, seed_e, cap_e - 1, D)
+            k_idx_e = torch.empty((B, cap_e, d_I), dtype=torch.bfloat16, device=dev)
+            for b in range(B):
+                rows = torch.empty((1, cap_e, d_I), dtype=torch.bfloat16, device=dev)
+                ci.fill_gaussian_(rows, seed_e, ci.TID_K_IDX, first=b * cap_e * d_I)
+                k_idx_e[b] = K.tile_indexer_cache(rows)[0]
+                del rows
+            self.enc_caches.append(DecodeCache(codes_e, scales_e, k_idx_e,
+                                               torch.full((B,), cap_e, dtype=torch.int32, device=dev),
+                                               torch.full((B,), W, dtype=torch.int32, device=dev)))
+            dst_e = torch.arange(B, device=dev, dtype=torch.int64) * cap_e + (cap_e - 1)
+            self.enc_writes.append((
+                ci.gaussian_rows(seed_e, ci.TID_KV, dst_e, D, dtype=torch.bfloat16, clip=ci.NORM_BOUND),
+                ci.gaussian_rows(seed_e, ci.TID_K_IDX, dst_e, d_I, dtype=torch.bfloat16), dst_e))
         self.layers = []
         for li, mode in enumerate(w.schedule):
             q = ci.gaussian(seed, ci.layer_tid(ci.TID_Q, li), (B, H, D), torch.bfloat16, dev)
             swa = ci.gaussian(seed, ci.layer_tid(ci.TID_SWA, li), (B, W, D), torch.bfloat16, dev)
             qi = wt = None
-            if mode in "FX":
+            if mode in "FXE":
                 qi = ci.gaussian(seed, ci.layer_tid(ci.TID_Q_IDX, li), (B, 1, H_I, d_I), torch.bfloat16, dev)
                 wt = ci.uniform(seed, ci.layer_tid(ci.TID_W, li), (B, 1, H_I), dev)
             self.layers.append(LayerInputs(q=q, swa=swa, q_idx=qi, w=wt))
@@ -99,10 +124,13 @@ class InputSet:
 def make_step(K, w: ci.Workload, s: InputSet, pool=None):
     from compressed_sparse_attention_05_amd.decode import DecodeStep
     has_full = "F" in w.schedule
+    has_enc = "E" in w.schedule
     return DecodeStep(w.schedule, s.cache, s.layers, k=w.k, P_b=w.P_b,
                       new_kv=s.new_kv if has_full else None,
                       new_kidx=s.new_kidx if has_full else None,
-                      dst_row=s.dst_row if has_full else None, pool=pool)
+                      dst_row=s.dst_row if has_full else None, pool=pool,
+                      enc_caches=s.enc_caches, enc_q_pos=s.enc_q_pos if has_enc else None, enc_m=w.enc_m,
+                      enc_writes=s.enc_writes if has_enc else None)
 
 
 def build_pool_for(K, w: ci.Workload, s: InputSet):
@@ -129,14 +157,17 @@ def algorithmic_bytes_per_query(w: ci.Workload):
     per_layer_attn = w.k * row + w.W * D * 2 + w.H * D * 2 + w.H * D * 4 + w.k * 4
     idx_q = w.H_I * d_I * 2 + w.H_I * 4
     total = 0
+    written = row + d_I * 2 + D * 2 + d_I * 2     # one written entry (read + write)
     for mode in w.schedule:
         if mode == "F":
             total += w.N * d_I * 2 + idx_q
+        elif mode == "E":
+            total += (w.N // w.enc_m) * d_I * 2 + idx_q + written
         elif mode == "X":
             total += w.P_b * 8 * d_I * 2 + w.P_b * 4 + idx_q
         total += per_layer_attn
     if "F" in w.schedule:
-        total += row + d_I * 2 + D * 2 + d_I * 2   # the written entry (read + write)
+        total += written
     return total
 
 
@@ -428,10 +459,11 @@ def main(argv=None):
         }
     if args.secondary:
         sec = []
-        # (workload, input sets, timed steps): the 20-layer step moves ~19 GB,
-        # far beyond the MALL, so one input set suffices there
+        # (workload, input sets, timed steps): the 20- and 38-layer steps move
+        # ~19 and ~46 GB, far beyond the MALL, so one input set suffices there
         for name, n_sets, steps2 in ((ci.DECODE_1M_BLOCK2.name, 2, max(20, args.steps // 4)),
-                                     (ci.DECODE_1M_20L.name, 1, 10)):
+                                     (ci.DECODE_1M_20L.name, 1, 10),
+                                     (ci.DECODE_1M_38L.name, 1, 5)):
             w2 = ci.WORKLOADS[name]
             del r
             torch.cuda.empty_cache()

@@ -7,9 +7,18 @@ Layer modes ("DeepSeek-V4.1-Flash KV Cache Compression" notes, section 2;
               over 8 positions, top 2,048 blocks; notes section 3).
   X  Reindex: score only the pool with the layer's own indexer query, take
               top-k inside it, attend.
-  R  Reuse:   attend with the index list of the preceding F or X layer.
-Every layer attends with its own query and its own sliding-window KV; all
-layers read the same MXFP4 main-KV cache and indexer-K cache.
+  R  Reuse:   attend with the index list (and KV set) of the preceding F,
+              X or E layer.
+  E  encoder Full: the same as F over an encoder KV set of its own, whose
+              entries each compress m = 2 tokens, so the token at absolute
+              position i sees min(ctx_len, floor((i + 1) / m)) entries (notes
+              section 2: the encoder compresses every m tokens and only
+              complete entries are visible).  It builds no pool (the encoder
+              has no Reindex layers); its top-k is taken inside a pool of
+              its own block maxima, which is exact for k <= P_b.
+Every layer attends with its own query and its own sliding-window KV; the
+decoder's layers read the decoder's MXFP4 main-KV and indexer-K caches, an
+encoder Full layer and the Reuse layers after it read that layer's set.
 
 DecodeStep pre-binds the ctypes argument structs of every library call of a
 step once, so a step costs one C call per kernel group and no Python-side
@@ -65,8 +74,23 @@ class DecodeStep:
                  P_b: int = 2048, new_kv: Optional[torch.Tensor] = None,
                  new_kidx: Optional[torch.Tensor] = None, dst_row: Optional[torch.Tensor] = None,
                  pool: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
-                 build_pool: bool = True, mfma_select: bool = False):
+                 build_pool: bool = True, mfma_select: bool = False,
+                 enc_caches: Optional[List[DecodeCache]] = None, enc_q_pos: Optional[torch.Tensor] = None,
+                 enc_m: int = 2, enc_writes: Optional[List[Optional[tuple]]] = None):
+        """enc_caches: one KV set per E layer, in schedule order.
+        enc_q_pos: [B] int64 absolute position of the token in each sequence
+        (E layers' visibility).  enc_writes: per E layer, None or
+        (new_kv [B][D], new_kidx [B][d_I], dst_row [B] int64) for an entry
+        the token completes, written before any scoring."""
         assert len(schedule) == len(layers)
+        n_enc = schedule.count("E")
+        enc_caches = list(enc_caches or [])
+        if len(enc_caches) != n_enc:
+            raise ValueError(f"schedule has {n_enc} encoder Full layers but {len(enc_caches)} encoder caches")
+        if n_enc and enc_q_pos is None:
+            raise ValueError("encoder Full layers need enc_q_pos")
+        if enc_writes is not None and len(enc_writes) != n_enc:
+            raise ValueError("enc_writes needs one entry per encoder Full layer")
         self.schedule, self.cache, self.layers, self.k, self.P_b = schedule, cache, layers, k, P_b
         B, cap, half = cache.codes.shape
         D = half * 2
@@ -86,6 +110,16 @@ class DecodeStep:
                     n_cache_rows, bd._ptr(cache.codes), bd._ptr(cache.scales), bd._ptr(new_kidx), kdt,
                     d_I if new_kidx is not None else 0, bd._ptr(cache.k_idx), None)
             self.calls.append(("write", self.L.mxfp4_kv_write, args))
+        for ei, wr in enumerate(enc_writes or []):
+            if wr is None:
+                continue
+            ec = enc_caches[ei]
+            e_kv, e_kidx, e_dst = wr
+            e_cap = ec.codes.shape[1]
+            args = (bd._ptr(e_kv), bd._dtype(e_kv, "enc new_kv"), e_kv.shape[0], D, bd._ptr(e_dst),
+                    B * e_cap, bd._ptr(ec.codes), bd._ptr(ec.scales), bd._ptr(e_kidx),
+                    bd._dtype(e_kidx, "enc new_kidx"), ec.k_idx.shape[-1], bd._ptr(ec.k_idx), None)
+            self.calls.append((f"write_enc{ei}", self.L.mxfp4_kv_write, args))
 
         self.scores = torch.empty((B, 1, cap), dtype=torch.float32, device=dev)
         self.block_max = torch.empty((B, 1, (cap + 7) // 8), dtype=torch.float32, device=dev)
@@ -95,8 +129,18 @@ class DecodeStep:
         self.idx_bufs = []
         pool_built = pool is not None
         cur_idx = None
+        cur_cache = cache
+        n_e = 0
         for li, (mode, lay) in enumerate(zip(schedule, layers)):
+            if mode == "E":
+                ec = enc_caches[n_e]
+                n_e += 1
+                cur_idx = self._encoder_full(li, lay, ec, enc_q_pos, enc_m, k, P_b)
+                cur_cache = ec
+                self._attn(li, lay, cur_idx, cur_cache)
+                continue
             if mode in "FX":
+                cur_cache = cache
                 idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
                 self.idx_bufs.append(idx)
                 use_pool = mode == "X"
@@ -119,7 +163,7 @@ class DecodeStep:
                                        (ctypes.byref(da), bd._ptr(dws), dn, None)))
                     pool_built = True
                     cur_idx = idx
-                    self._attn(li, lay, cur_idx)
+                    self._attn(li, lay, cur_idx, cur_cache)
                     continue
                 sa = bd.ScoreArgs(
                     q_idx=lay.q_idx.data_ptr(), q_dtype=bd._dtype(lay.q_idx, "q_idx"), w=lay.w.data_ptr(),
@@ -172,13 +216,63 @@ class DecodeStep:
                 cur_idx = idx
             elif mode == "R":
                 if cur_idx is None:
-                    raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
+                    raise ValueError("a Reuse layer needs an earlier Full, Reindex or encoder Full layer")
             else:
                 raise ValueError(f"unknown layer mode {mode!r}")
-            self._attn(li, lay, cur_idx)
+            self._attn(li, lay, cur_idx, cur_cache)
 
-    def _attn(self, li: int, lay: "LayerInputs", cur_idx: torch.Tensor) -> None:
-        cache, B, cap, D, k = self.cache, self.B, self.cap, self.D, self.k
+    def _encoder_full(self, li: int, lay: "LayerInputs", ec: DecodeCache, q_pos: torch.Tensor, m: int,
+                      k: int, P_b: int) -> torch.Tensor:
+        """Score every visible entry of the encoder set (q_pos, m visibility),
+        then its top-k; returns the index buffer."""
+        B = self.B
+        dev = ec.codes.device
+        e_cap = ec.codes.shape[1]
+        d_I = ec.k_idx.shape[-1]
+        nb = (e_cap + 7) // 8
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+        self.idx_bufs.append(idx)
+        scores = torch.empty((B, 1, e_cap), dtype=torch.float32, device=dev)
+        bm = torch.empty((B, 1, nb), dtype=torch.float32, device=dev)
+        qp = q_pos.to(device=dev, dtype=torch.int64).reshape(B, 1).contiguous()
+        inner = k <= P_b and 8 * P_b <= 32768        # top-k inside a pool of its own
+        sa = bd.ScoreArgs(
+            q_idx=lay.q_idx.data_ptr(), q_dtype=bd._dtype(lay.q_idx, "q_idx"), w=lay.w.data_ptr(),
+            k_idx=ec.k_idx.data_ptr(), k_dtype=bd._dtype(ec.k_idx, "k_idx"), B=B, Tq=1,
+            cap=e_cap, H_I=lay.q_idx.shape[2], d_I=d_I, ctx_len=ec.ctx_len.data_ptr(), q_pos=qp.data_ptr(),
+            m=m, pool_blocks=None, P_b=0, scores=scores.data_ptr(), ld_scores=e_cap,
+            block_max=bm.data_ptr() if inner else None)
+        nws = self.L.csa2_index_score_workspace_size(ctypes.byref(sa))
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        self._keep += [sa, ws, scores, bm, qp]
+        self.calls.append((f"score{li}", self.L.csa2_index_score, (ctypes.byref(sa), bd._ptr(ws), nws, None)))
+        if inner:
+            epool = torch.empty((B, 1, P_b), dtype=torch.int32, device=dev)
+            self._keep.append(epool)
+            if P_b <= 2048 and nb <= 32768:
+                self.calls.append((f"pool{li}", self.L.csa2_pool_topk,
+                                   (bd._ptr(bm), B, nb, nb, P_b, bd._ptr(epool), bd._ptr(scores), e_cap, k,
+                                    bd._ptr(idx), None)))
+            else:
+                pws_n = self.L.csa2_build_candidate_pool_workspace_size(B, nb, P_b)
+                pws = torch.empty(max(pws_n, 256), dtype=torch.uint8, device=dev)
+                self._keep.append(pws)
+                self.calls.append((f"pool{li}", self.L.csa2_build_candidate_pool,
+                                   (bd._ptr(bm), B, nb, nb, P_b, bd._ptr(epool), bd._ptr(pws), pws_n, None)))
+                self.calls.append((f"topk{li}", self.L.csa2_topk_from_pool,
+                                   (bd._ptr(scores), B, e_cap, bd._ptr(epool), P_b, k, bd._ptr(idx), None)))
+        else:
+            tws_n = self.L.csa2_topk_workspace_size(B, e_cap, k)
+            tws = torch.empty(max(tws_n, 256), dtype=torch.uint8, device=dev)
+            self._keep.append(tws)
+            self.calls.append((f"topk{li}", self.L.csa2_topk,
+                               (bd._ptr(scores), B, e_cap, e_cap, k, None, 0, bd._ptr(idx), bd._ptr(tws),
+                                tws_n, None)))
+        return idx
+
+    def _attn(self, li: int, lay: "LayerInputs", cur_idx: torch.Tensor, cache: DecodeCache) -> None:
+        B, D, k = self.B, self.D, self.k
+        cap = cache.codes.shape[1]
         aa = bd.AttnArgs(q=lay.q.data_ptr(), q_dtype=bd._dtype(lay.q, "q"), codes=cache.codes.data_ptr(),
                          scales=cache.scales.data_ptr(), cap=cap, idx=cur_idx.data_ptr(), k=k,
                          swa=lay.swa.data_ptr(), swa_dtype=bd._dtype(lay.swa, "swa"), W=lay.swa.shape[1],

@@ -158,12 +158,13 @@ class Workload:
     k: int            # top-k
     W: int            # sliding window
     m: int            # tokens per compressed entry
-    schedule: str     # F = Full, X = Reindex, R = Reuse (one letter per layer)
+    schedule: str     # F = Full, X = Reindex, R = Reuse, E = encoder Full (one letter per layer)
     P_b: int = 2048   # candidate-pool blocks (8 positions each)
     T: int = 1        # query tokens per sequence (prefill chunk length)
     prior_tokens: int = 0
     fp32: bool = False
     seed: int = 1000
+    enc_m: int = 2    # tokens per entry of an encoder KV set (E layers)
 
 
 TINY = Workload("tiny-full-1k", B=1, N=1024, D=64, d_I=32, H_I=2, H=4, k=64, W=32, m=1,
@@ -178,4 +179,11 @@ PREFILL_CHUNK = Workload("prefill-chunk-m2-t8192", B=1, N=135168, D=512, d_I=128
 DECODE_1M_20L = Workload("decode-20layer-1M-b64", B=64, N=1048576, D=512, d_I=128, H_I=8, H=64,
                          k=2048, W=128, m=1, schedule="FRRR" + "XRRR" * 4, seed=1005)
 
-WORKLOADS = {w.name: w for w in (TINY, DECODE_128K, DECODE_1M_BLOCK2, PREFILL_CHUNK, DECODE_1M_20L)}
+# one decode token through every CSA2 layer of the network: the encoder's
+# three blocks of Full + 5 Reuse at m = 2 (each Full over a KV set of its own,
+# 524,288 entries at 1M tokens), then the decoder's 20 layers
+DECODE_1M_38L = Workload("decode-38layer-1M-b64", B=64, N=1048576, D=512, d_I=128, H_I=8, H=64,
+                         k=2048, W=128, m=1, schedule="ERRRRR" * 3 + "FRRR" + "XRRR" * 4, seed=1006)
+
+WORKLOADS = {w.name: w for w in (TINY, DECODE_128K, DECODE_1M_BLOCK2, PREFILL_CHUNK, DECODE_1M_20L,
+                                 DECODE_1M_38L)}

@@ -87,3 +87,88 @@ def test_decode_step_full_reindex_reuse(K, k, P_b, mfma):
             want = oracle.attn_decode(q[b], oc, osc, oidx, swa[b], swa_len[b], sm)
             err = float(np.max(np.abs(step.outs[li][b].cpu().numpy() - want)))
             assert err < ATOL, (b, li, err)
+
+
+def test_decode_step_encoder_full_m2(K):
+    # schedule F R E R: a decoder Full layer and its Reuse, then an encoder
+    # Full layer over its own KV set at m = 2 and a Reuse of it.  Sequence 0's
+    # token (position 19,999) completes encoder entry 9,999, written by the
+    # step; sequence 1's token (position 15,000) completes none, and its
+    # encoder set holds entries past floor((i + 1) / 2) = 7,500 that must stay
+    # invisible.
+    from compressed_sparse_attention_05_amd.decode import DecodeCache, DecodeStep, LayerInputs
+    dev = torch.device("cuda:0")
+    B, cap, cap_e, D, H, d_I, H_I, W, k, P_b = 2, 20032, 10048, 512, 64, 128, 8, 128, 256, 512
+    ctx = [20000, 15001]
+    pos = [19999, 15000]
+    ctx_e = [10000, 8000]
+    vis_e = [oracle.prefill_vis(pos[b], ctx_e[b], 2) for b in range(B)]
+    assert vis_e == [10000, 7500]
+    swa_len = [128, 90]
+    seed = 433
+    kv = ci.gaussian(seed, ci.TID_KV, (B, cap, D), clip=ci.NORM_BOUND)
+    kidx = ci.gaussian(seed, ci.TID_K_IDX, (B, cap, d_I), dtype=torch.bfloat16)
+    kv_e = ci.gaussian(seed + 50, ci.TID_KV, (B, cap_e, D), clip=ci.NORM_BOUND)
+    kidx_e = ci.gaussian(seed + 50, ci.TID_K_IDX, (B, cap_e, d_I), dtype=torch.bfloat16)
+
+    def make_cache(kv_, kidx_, cap_, n_rows, skip):
+        codes = torch.zeros((B, cap_, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.zeros((B, cap_, D // 16), dtype=torch.uint8, device=dev)
+        rows = torch.cat([torch.tensor([b * cap_ + r for r in range(n_rows[b]) if (b, r) not in skip],
+                                       dtype=torch.int64) for b in range(B)]).to(dev)
+        flat = kv_.reshape(B * cap_, D).to(dev)
+        K.mxfp4_kv_write(flat[rows], rows, codes, scales)
+        krows = kidx_.clone()
+        for b in range(B):
+            krows[b, n_rows[b]:] = 0
+        for (b, r) in skip:
+            krows[b, r] = 0
+        return codes, scales, K.tile_indexer_cache(krows.to(dev)), flat
+
+    dec_new = [(0, ctx[0] - 1), (1, ctx[1] - 1)]
+    enc_new = [(0, ctx_e[0] - 1)]
+    codes, scales, kcache, flat_kv = make_cache(kv, kidx, cap, ctx, set(dec_new))
+    codes_e, scales_e, kcache_e, flat_kv_e = make_cache(kv_e, kidx_e, cap_e, ctx_e, set(enc_new))
+    sl = torch.tensor(swa_len, dtype=torch.int32, device=dev)
+    cache = DecodeCache(codes=codes, scales=scales, k_idx=kcache,
+                        ctx_len=torch.tensor(ctx, dtype=torch.int32, device=dev), swa_len=sl)
+    ecache = DecodeCache(codes=codes_e, scales=scales_e, k_idx=kcache_e,
+                         ctx_len=torch.tensor(ctx_e, dtype=torch.int32, device=dev), swa_len=sl)
+    layers = []
+    for li in range(4):
+        q = ci.gaussian(seed + li, ci.TID_Q, (B, H, D), dtype=torch.bfloat16)
+        swa = ci.gaussian(seed + li, ci.TID_SWA, (B, W, D), dtype=torch.bfloat16)
+        qi = ci.gaussian(seed + li, ci.TID_Q_IDX, (B, 1, H_I, d_I), dtype=torch.bfloat16)
+        wi = ci.uniform(seed + li, ci.TID_W, (B, 1, H_I))
+        layers.append((q, swa, qi, wi))
+    lin = [LayerInputs(q=q.to(dev), swa=swa.to(dev), q_idx=qi.to(dev), w=wi.to(dev)) for q, swa, qi, wi in layers]
+    d_rows = torch.tensor([b * cap + r for b, r in dec_new], dtype=torch.int64)
+    e_rows = torch.tensor([b * cap_e + r for b, r in enc_new], dtype=torch.int64)
+    step = DecodeStep("FRER", cache, lin, k=k, P_b=P_b,
+                      new_kv=flat_kv[d_rows.to(dev)].contiguous(),
+                      new_kidx=kidx.reshape(B * cap, d_I)[d_rows].contiguous().to(dev), dst_row=d_rows.to(dev),
+                      enc_caches=[ecache], enc_q_pos=torch.tensor(pos, dtype=torch.int64, device=dev),
+                      enc_writes=[(flat_kv_e[e_rows.to(dev)].contiguous(),
+                                   kidx_e.reshape(B * cap_e, d_I)[e_rows].contiguous().to(dev), e_rows.to(dev))])
+    step.run()
+    torch.cuda.synchronize()
+    sm = 1.0 / math.sqrt(D)
+    idx_f = step.idx_bufs[0].cpu().numpy()
+    idx_e = step.idx_bufs[1].cpu().numpy()
+    for b in range(B):
+        q0, s0, qi0, wi0 = layers[0]
+        sc = oracle.full_scores(qi0[b, 0], wi0[b, 0], kidx[b], ctx[b], cap)
+        of = oracle.topk(sc, k)
+        assert np.array_equal(idx_f[b, 0], of), b
+        q2, s2, qi2, wi2 = layers[2]
+        sce = oracle.full_scores(qi2[b, 0], wi2[b, 0], kidx_e[b], vis_e[b], cap_e)
+        oe = oracle.topk(sce, k)
+        assert np.array_equal(idx_e[b, 0], oe), b
+        assert oe.max() < vis_e[b]
+        oc, osc = oracle.mxfp4_encode(kv[b, :ctx[b]])
+        oce, osce = oracle.mxfp4_encode(kv_e[b, :vis_e[b]])
+        for li, oidx, (c_, s_) in ((0, of, (oc, osc)), (1, of, (oc, osc)), (2, oe, (oce, osce)), (3, oe, (oce, osce))):
+            q, swa = layers[li][0], layers[li][1]
+            want = oracle.attn_decode(q[b], c_, s_, oidx, swa[b], swa_len[b], sm)
+            err = float(np.max(np.abs(step.outs[li][b].cpu().numpy() - want)))
+            assert err < ATOL, (b, li, err)
