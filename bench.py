@@ -301,6 +301,55 @@ def run_prefill(K, w: ci.Workload, steps: int, warmup: int, dev):
             "attn_mfma_frac": round(attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def run_replay(K, w: ci.Workload, steps: int, warmup: int, dev):
+    """SWA bounded replay: the decoder's layers over the newest T tokens of
+    one sequence (positions prior_tokens .. prior_tokens + T - 1), every
+    token a decoder query with its own pool, windows cut at the replay start.
+    The replayed tokens' global KV is already cached."""
+    from compressed_sparse_attention_05_amd.replay import DecoderReplay, ReplayLayer
+    seed, N, D, d_I, T, W, H = w.seed, w.N, w.D, w.d_I, w.T, w.W, w.H
+    codes = torch.empty((1, N, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((1, N, D // 16), dtype=torch.uint8, device=dev)
+    fill_kv_cache(K, codes, scales, seed, N, D)
+    rows = torch.empty((1, N, d_I), dtype=torch.bfloat16, device=dev)
+    ci.fill_gaussian_(rows, seed, ci.TID_K_IDX)
+    k_idx = K.tile_indexer_cache(rows)[0]
+    del rows
+    layers = []
+    for li, mode in enumerate(w.schedule):
+        lay = ReplayLayer(q=ci.gaussian(seed, ci.layer_tid(ci.TID_Q, li), (T, H, D), torch.bfloat16, dev),
+                          swa=ci.gaussian(seed, ci.layer_tid(ci.TID_SWA, li), (T + W - 1, D), torch.bfloat16, dev))
+        if mode in "FX":
+            lay.q_idx = ci.gaussian(seed, ci.layer_tid(ci.TID_Q_IDX, li), (T, w.H_I, d_I), torch.bfloat16, dev)
+            lay.w = ci.uniform(seed, ci.layer_tid(ci.TID_W, li), (T, w.H_I), dev)
+        layers.append(lay)
+    rp = DecoderReplay(w.schedule, codes[0], scales[0], k_idx, N, w.prior_tokens, w.k, W, layers, P_b=w.P_b)
+    for _ in range(warmup):
+        rp.run()
+    torch.cuda.synchronize()
+    names = [f"score{i}" for i, mode in enumerate(w.schedule) if mode in "FX"]
+    names += [f"attn{i}" for i in range(len(w.schedule))]
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        rp.run(events=evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    full_ms = sum(e["score0"][0].elapsed_time(e["score0"][1]) for e in evs) / steps
+    attn_ms = sum(e[n][0].elapsed_time(e[n][1]) for e in evs for n in names if n.startswith("attn")) / steps
+    # the Full layer's keys once (every token shares them), Reindex pools and
+    # attention gathers per token
+    scan_b = N * d_I * 2
+    return {"workload": w.name, "tokens": T, "context": N, "schedule": w.schedule,
+            "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 3),
+            "full_scan_ms": round(full_ms, 3),
+            "full_scan_GBps_per_token": round(T * scan_b / (full_ms * 1e-3) / 1e9, 1),
+            "attn_ms": round(attn_ms, 3)}
+
+
 def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
     """The oracle, as it stands, on n_queries sequences of the workload's
     first Full layer (write + scan + block max + pool + top-k + attention).
@@ -380,6 +429,8 @@ def main(argv=None):
     ap.add_argument("--cpu-queries", type=int, default=8, help="oracle sample size (0 = skip)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time the prefill chunk workload (profiling)")
+    ap.add_argument("--replay-only", action="store_true",
+                    help="only time the decoder replay workload (profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
@@ -402,6 +453,9 @@ def main(argv=None):
         return 0
     if args.prefill_only:
         print(json.dumps(run_prefill(K, ci.PREFILL_CHUNK, args.steps, args.warmup, dev)), flush=True)
+        return 0
+    if args.replay_only:
+        print(json.dumps(run_replay(K, ci.DECODER_REPLAY, args.steps, args.warmup, dev)), flush=True)
         return 0
     w = ci.WORKLOADS[args.workload]
     if "F" not in w.schedule:
@@ -486,6 +540,9 @@ def main(argv=None):
         torch.cuda.empty_cache()
         print(f"# setting up {ci.PREFILL_CHUNK.name}", file=sys.stderr, flush=True)
         sec.append(run_prefill(K, ci.PREFILL_CHUNK, 3, 1, dev))
+        torch.cuda.empty_cache()
+        print(f"# setting up {ci.DECODER_REPLAY.name}", file=sys.stderr, flush=True)
+        sec.append(run_replay(K, ci.DECODER_REPLAY, 3, 1, dev))
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
     return 0

@@ -1,6 +1,6 @@
 """Host-side composition of one prefill chunk through an encoder layer schedule.
 
-An encoder block ("DeepSeek-V4.1-Flash KV Cache Compression" notes, section 1;
+An encoder block ("DeepSeek-V4.1-Flash KV Cache Compression" notes, section 2;
 "...reading a model through its three memory costs", section 03) has one
 Full layer followed by Reuse layers (schedule "FRRRRR").  For a chunk of T
 query tokens at positions q_pos0 .. q_pos0+T-1 with m tokens per entry:

@@ -185,5 +185,12 @@ DECODE_1M_20L = Workload("decode-20layer-1M-b64", B=64, N=1048576, D=512, d_I=12
 DECODE_1M_38L = Workload("decode-38layer-1M-b64", B=64, N=1048576, D=512, d_I=128, H_I=8, H=64,
                          k=2048, W=128, m=1, schedule="ERRRRR" * 3 + "FRRR" + "XRRR" * 4, seed=1006)
 
+# SWA bounded replay: the decoder's 20 layers over the newest n_win = 128
+# tokens of one 1M-token sequence, each token a decoder query with its own
+# candidate pool, windows cut at the replay start
+DECODER_REPLAY = Workload("decoder-replay-1M-t128", B=1, N=1048576, D=512, d_I=128, H_I=8, H=64,
+                          k=2048, W=128, m=1, schedule="FRRR" + "XRRR" * 4, T=128,
+                          prior_tokens=1048576 - 128, seed=1007)
+
 WORKLOADS = {w.name: w for w in (TINY, DECODE_128K, DECODE_1M_BLOCK2, PREFILL_CHUNK, DECODE_1M_20L,
-                                 DECODE_1M_38L)}
+                                 DECODE_1M_38L, DECODER_REPLAY)}
