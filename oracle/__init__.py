@@ -61,6 +61,8 @@ def lib():
             "csa2o_prefill_vis": (i64, [i64, i64, i32]),
             "csa2o_prefill_scores": (None, [P, P, P, i32, i32, P, i64, i64, i32, i64, P]),
             "csa2o_attn_prefill": (None, [P, i64, i32, i32, P, P, P, i32, P, i32, i64, i64, dbl, P]),
+            "csa2o_bf16_nearest": (ctypes.c_uint16, [ctypes.c_float]),
+            "csa2o_project_kidx": (None, [P, i64, i32, P, i32, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -119,6 +121,24 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     n, half = codes.shape
     out = np.zeros((n, half * 2), np.float64)
     lib().csa2o_mxfp4_decode(_ptr(codes), _ptr(scales), n, half * 2, _ptr(out))
+    return out
+
+
+def bf16_nearest(f: float) -> int:
+    """bfloat16 bit pattern nearest to a finite float32 (ties to even)."""
+    return lib().csa2o_bf16_nearest(float(np.float32(f)))
+
+
+def project_kidx(x, W) -> np.ndarray:
+    """Indexer-K rows from latent rows: x [n][D], W [D][d_I] float32 ->
+    bfloat16 bit patterns [n][d_I] (fp32 fma chain over channels, then
+    round to nearest bfloat16)."""
+    x, W = as_f32(x), as_f32(W)
+    n, D = x.shape
+    d_I = W.shape[1]
+    assert W.shape[0] == D
+    out = np.zeros((n, d_I), np.uint16)
+    lib().csa2o_project_kidx(_ptr(x), n, D, _ptr(W), d_I, _ptr(out))
     return out
 
 

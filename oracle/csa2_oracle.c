@@ -124,6 +124,46 @@ void csa2o_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, int64_t n_r
 }
 
 /* ------------------------------------------------------------------------ */
+/* Indexer-K projection.  A Full layer projects its indexer K directly from  */
+/* its main KV ([KVC] section 2).  The pages give neither the weights nor    */
+/* the precision; this library reads it as a projection of the latent row   */
+/* before MXFP4 encoding (the row the entry is made from), with float32     */
+/* weights W[D][d_I]:                                                        */
+/*   acc = +0; for c = 0..D-1: acc = fma(x[c], W[c][j], acc)                 */
+/*   k[j] = acc rounded to bfloat16 (nearest, ties to the even mantissa)     */
+/* ------------------------------------------------------------------------ */
+
+/* The bfloat16 nearest to a finite float: of the two bfloat16 values that
+ * bracket f (f with its low 16 bits cleared, and the next bfloat16 away
+ * from zero), the closer one; at equal distance the one whose last mantissa
+ * bit is 0.  Returns the bfloat16 bit pattern. */
+static uint16_t bf16_nearest(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lo = u & 0xffff0000u, hi = lo + 0x10000u;
+    float flo, fhi;
+    memcpy(&flo, &lo, 4);
+    memcpy(&fhi, &hi, 4);
+    double dlo = fabs((double)f - (double)flo), dhi = fabs((double)fhi - (double)f);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return ((lo >> 16) & 1u) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);
+}
+
+uint16_t csa2o_bf16_nearest(float f) { return bf16_nearest(f); }
+
+void csa2o_project_kidx(const float *x, int64_t n_rows, int D, const float *W, int d_I, uint16_t *out)
+{
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int j = 0; j < d_I; ++j) {
+            float acc = 0.0f;
+            for (int c = 0; c < D; ++c) acc = fmaf(x[r * D + c], W[(int64_t)c * d_I + j], acc);
+            out[r * d_I + j] = bf16_nearest(acc);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Indexer score.  The pages give no formula ([KVC] sections 2-3 say only   */
 /* that Full mode scores every visible entry with its own indexer Q against */
 /* an indexer K projected from main KV; [DR] section 03).  This library     */

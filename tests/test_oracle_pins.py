@@ -560,3 +560,75 @@ def test_full_topk_equals_topk_inside_pool_and_pool_through_superblocks():
         sel = oracle.topk(cand, P_b)
         pool2 = np.array([8 * sb[t // 8] + t % 8 if t >= 0 else -1 for t in sel], np.int32)
         assert np.array_equal(pool2, pool), trial
+
+
+# ---------------------------------------------------------------------------
+# Indexer-K projection (a Full layer projects indexer K from its main KV):
+# fp32 fma chain over the latent channels, then the nearest bfloat16.
+
+def _bf16_bits_torch(v: np.ndarray) -> np.ndarray:
+    # torch's float32 -> bfloat16 conversion (round to nearest, ties to even)
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_nearest_matches_library_conversion_and_ties():
+    g = np.random.default_rng(7)
+    vals = np.concatenate([g.standard_normal(4000).astype(np.float32) * 10.0 ** g.integers(-30, 30, 4000),
+                           np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38, 1e-40, -1e-40], np.float32)])
+    got = np.array([oracle.bf16_nearest(v) for v in vals], np.uint16)
+    assert np.array_equal(got, _bf16_bits_torch(vals))
+    # exact ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> the even one (1);
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6 -> the even one (1 + 2^-6)
+    assert oracle.bf16_nearest(1.0 + 2.0 ** -8) == 0x3F80
+    assert oracle.bf16_nearest(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert oracle.bf16_nearest(-(1.0 + 2.0 ** -8)) == 0xBF80
+
+
+def test_projection_one_hot_and_permutation_copy_the_latent():
+    g = np.random.default_rng(11)
+    D, d_I, n = 512, 128, 5
+    x = torch.from_numpy(g.standard_normal((n, D)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    W = np.zeros((D, d_I), np.float32)
+    W[np.arange(d_I), np.arange(d_I)] = 1.0
+    assert np.array_equal(oracle.project_kidx(x, W), _bf16_bits_torch(x[:, :d_I]))
+    perm = g.permutation(D)[:d_I]
+    W = np.zeros((D, d_I), np.float32)
+    W[perm, np.arange(d_I)] = 1.0
+    assert np.array_equal(oracle.project_kidx(x, W), _bf16_bits_torch(x[:, perm]))
+    # a scaled column: k[j] = 2^-3 * x[perm[j]] exactly
+    W *= 0.125
+    assert np.array_equal(oracle.project_kidx(x, W), _bf16_bits_torch(x[:, perm] * 0.125))
+
+
+def test_projection_exactly_summable_equals_float64_matmul():
+    # x and W on a 2^-3 grid within +-4: every partial sum is a multiple of
+    # 2^-6 below 2^13, exact in float32 in any order, so the chain equals the
+    # float64 matrix product, and the rounding is the library's conversion
+    g = np.random.default_rng(13)
+    D, d_I, n = 512, 128, 7
+    x = np.clip(np.round(g.standard_normal((n, D)) * 8) / 8, -4, 4).astype(np.float32)
+    W = np.clip(np.round(g.standard_normal((D, d_I)) * 8) / 8, -4, 4).astype(np.float32)
+    exact = x.astype(np.float64) @ W.astype(np.float64)
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    assert np.array_equal(oracle.project_kidx(x, W), _bf16_bits_torch(exact.astype(np.float32)))
+
+
+def test_projection_chain_is_fused_and_forward():
+    D, d_I = 16, 8
+    # fused: channel 0 puts -(1 + 2^-22) in the accumulator, channel 1 adds
+    # (1 + 2^-23)^2 = 1 + 2^-22 + 2^-46; one rounding leaves exactly 2^-46
+    # (bfloat16 0x2880), a rounded product first would leave 0
+    x = np.zeros((1, D), np.float32)
+    W = np.zeros((D, d_I), np.float32)
+    x[0, 0], W[0, 0] = 1.0, -(1.0 + 2.0 ** -22)
+    x[0, 1] = W[1, 0] = 1.0 + 2.0 ** -23
+    out = oracle.project_kidx(x, W)
+    assert out[0, 0] == 0x2880 and np.all(out[0, 1:] == 0)
+    # forward order: 2^30 + 1 rounds to 2^30 in float32, then -2^30 cancels
+    # to +0; a chain run from the last channel would give exactly 1 (0x3F80)
+    x = np.zeros((1, D), np.float32)
+    W = np.zeros((D, d_I), np.float32)
+    x[0, 0], W[0, 0] = 2.0 ** 30, 1.0
+    x[0, 1], W[1, 0] = 1.0, 1.0
+    x[0, 2], W[2, 0] = 2.0 ** 30, -1.0
+    assert oracle.project_kidx(x, W)[0, 0] == 0
