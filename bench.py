@@ -350,6 +350,40 @@ def run_replay(K, w: ci.Workload, steps: int, warmup: int, dev):
             "attn_ms": round(attn_ms, 3)}
 
 
+def run_project(K, dev, reps: int = 50):
+    """The MXFP4 write with the indexer key projected from the latent row
+    (csa2_kv_write_project, D = 512 -> d_I = 128 bfloat16), against the plain
+    write that copies a given key row, for one decode token of 64 sequences
+    and for the 4,096 entries of an m = 2 prefill chunk of 8,192 tokens."""
+    D, d_I = 512, 128
+    w_ik = (ci.gaussian(7, ci.TID_W_IK, (D, d_I)) * (1.0 / math.sqrt(D))).to(dev)
+    res = {"workload": "kv-write-project", "latent": D, "indexer": f"{d_I} bf16"}
+    for label, n, cap in (("decode_b64", 64, 65536), ("prefill_chunk_4096", 4096, 65536)):
+        x = ci.gaussian(8, ci.TID_KV, (n, D), dtype=torch.bfloat16, clip=ci.NORM_BOUND).to(dev)
+        kr = ci.gaussian(8, ci.TID_K_IDX, (n, d_I), dtype=torch.bfloat16).to(dev)
+        dst = torch.arange(n, dtype=torch.int64, device=dev) * (cap // n)
+        codes = torch.zeros((cap, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.zeros((cap, D // 16), dtype=torch.uint8, device=dev)
+        kc = torch.zeros((cap, d_I), dtype=torch.bfloat16, device=dev)
+        timings = {}
+        for name, fn in (("project", lambda: K.csa2_kv_write_project(x, dst, codes, scales, w_ik, kc)),
+                         ("copy", lambda: K.mxfp4_kv_write(x, dst, codes, scales, kr, kc))):
+            for _ in range(5):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            timings[name] = a.elapsed_time(b) / reps * 1e3
+        res[label] = {"rows": n, "project_us": round(timings["project"], 2),
+                      "copy_us": round(timings["copy"], 2),
+                      "project_TFLOPs_fp32": round(2.0 * n * D * d_I / (timings["project"] * 1e-6) / 1e12, 2)}
+    return res
+
+
 def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
     """The oracle, as it stands, on n_queries sequences of the workload's
     first Full layer (write + scan + block max + pool + top-k + attention).
@@ -431,6 +465,8 @@ def main(argv=None):
                     help="only time the prefill chunk workload (profiling)")
     ap.add_argument("--replay-only", action="store_true",
                     help="only time the decoder replay workload (profiling)")
+    ap.add_argument("--project-only", action="store_true",
+                    help="only time the write with the projected indexer key (profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
@@ -456,6 +492,9 @@ def main(argv=None):
         return 0
     if args.replay_only:
         print(json.dumps(run_replay(K, ci.DECODER_REPLAY, args.steps, args.warmup, dev)), flush=True)
+        return 0
+    if args.project_only:
+        print(json.dumps(run_project(K, dev)), flush=True)
         return 0
     w = ci.WORKLOADS[args.workload]
     if "F" not in w.schedule:
@@ -543,6 +582,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         print(f"# setting up {ci.DECODER_REPLAY.name}", file=sys.stderr, flush=True)
         sec.append(run_replay(K, ci.DECODER_REPLAY, 3, 1, dev))
+        sec.append(run_project(K, dev))
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
     return 0

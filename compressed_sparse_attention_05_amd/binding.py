@@ -61,6 +61,7 @@ SIGNATURES = {
     "csa2_version": (ctypes.c_char_p, []),
     "csa2_last_error": (ctypes.c_char_p, []),
     "mxfp4_kv_write": (ctypes.c_int, [P, ctypes.c_int, i64, i32, P, i64, P, P, P, ctypes.c_int, i32, P, P]),
+    "csa2_kv_write_project": (ctypes.c_int, [P, ctypes.c_int, i64, i32, P, i64, P, P, P, i32, P, P]),
     "csa2_index_score_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScoreArgs)]),
     "csa2_index_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, ctypes.c_size_t, P]),
     "csa2_topk_workspace_size": (ctypes.c_size_t, [i64, i64, i32]),
@@ -187,6 +188,31 @@ def mxfp4_kv_write(x, dst_row, codes, scales, idx_k_rows=None, idx_k_cache=None,
     _check(lib().mxfp4_kv_write(_ptr(x), _dtype(x, "x"), n, D, _ptr(dst_row), n_cache_rows,
                                 _ptr(codes), _ptr(scales), _ptr(idx_k_rows), kdt, d_I,
                                 _ptr(idx_k_cache), _stream(stream)))
+
+
+def csa2_kv_write_project(x, dst_row, codes, scales, w_ik, idx_k_cache, stream=None):
+    """Quantise rows x [n][D] into codes/scales at flat rows dst_row (int64)
+    and write their projected indexer keys bf16(x . w_ik) (w_ik [D][d_I]
+    float32) into the tiled bfloat16 idx_k_cache."""
+    for t, nm in ((x, "x"), (dst_row, "dst_row"), (codes, "codes"), (scales, "scales"), (w_ik, "w_ik"),
+                  (idx_k_cache, "idx_k_cache")):
+        _dev(t, nm)
+    if dst_row.dtype != torch.int64 or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise TypeError("dst_row must be int64, codes/scales uint8")
+    if w_ik.dtype != torch.float32 or w_ik.dim() != 2 or not w_ik.is_contiguous():
+        raise TypeError("w_ik must be a contiguous float32 [D][d_I] tensor")
+    if idx_k_cache.dtype != torch.bfloat16:
+        raise TypeError("idx_k_cache must be bfloat16")
+    n, D = x.shape[0], x.shape[-1]
+    d_I = w_ik.shape[1]
+    if w_ik.shape[0] != D:
+        raise ValueError(f"w_ik has {w_ik.shape[0]} rows, x has {D} channels")
+    n_cache_rows = codes.numel() // (D // 2)
+    if scales.numel() != n_cache_rows * (D // 16) or idx_k_cache.numel() != n_cache_rows * d_I:
+        raise ValueError("codes, scales and idx_k_cache describe different row counts")
+    _check(lib().csa2_kv_write_project(_ptr(x), _dtype(x, "x"), n, D, _ptr(dst_row), n_cache_rows,
+                                       _ptr(codes), _ptr(scales), _ptr(w_ik), d_I, _ptr(idx_k_cache),
+                                       _stream(stream)))
 
 
 def csa2_index_score(q_idx, w, k_idx, ctx_len, *, q_pos=None, m: int = 1, pool_blocks=None,

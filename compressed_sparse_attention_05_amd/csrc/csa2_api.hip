@@ -77,6 +77,30 @@ int mxfp4_kv_write(const void* x, int x_dtype, int64_t n_rows, int32_t D, const 
 }
 
 // --------------------------------------------------------------------------
+int csa2_kv_write_project(const void* x, int x_dtype, int64_t n_rows, int32_t D, const int64_t* dst_row,
+                          int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const float* w_ik,
+                          int32_t d_I, void* idx_k_cache, void* stream) {
+    if (n_rows < 0) return fail(CSA2_E_INVALID, "csa2_kv_write_project: n_rows < 0");
+    if (D <= 0 || D % 16 != 0)
+        return fail(CSA2_E_INVALID, "csa2_kv_write_project: D=%d must be a positive multiple of 16", D);
+    if (d_I <= 0 || d_I % 8 != 0)
+        return fail(CSA2_E_INVALID, "csa2_kv_write_project: d_I=%d must be a positive multiple of 8", d_I);
+    if (!valid_dtype(x_dtype)) return fail(CSA2_E_INVALID, "csa2_kv_write_project: bad x_dtype %d", x_dtype);
+    if (n_cache_rows < 0 || n_cache_rows % 64 != 0)
+        return fail(CSA2_E_INVALID, "csa2_kv_write_project: the tiled indexer cache needs n_cache_rows %% 64 == 0");
+    if (!csa2::kv_project_shape_supported(D, d_I))
+        return fail(CSA2_E_UNSUPPORTED, "csa2_kv_write_project: (D=%d, d_I=%d) needs more than 64 KiB of LDS", D, d_I);
+    if (n_rows == 0) return ok();
+    if (!x || !dst_row || !codes || !scales || !w_ik || !idx_k_cache)
+        return fail(CSA2_E_INVALID, "csa2_kv_write_project: null pointer");
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(idx_k_cache, 16))
+        return fail(CSA2_E_INVALID, "csa2_kv_write_project: x and idx_k_cache must be 16-byte and codes 8-byte aligned");
+    hipError_t e = csa2::launch_kv_write_project(x, x_dtype == CSA2_BF16, n_rows, D, dst_row, n_cache_rows, codes,
+                                                 scales, w_ik, d_I, idx_k_cache, as_stream(stream));
+    return device_status(e, "csa2_kv_write_project");
+}
+
+// --------------------------------------------------------------------------
 static int check_score_args(const csa2_score_args* a) {
     if (!a) return fail(CSA2_E_INVALID, "csa2_index_score: args is null");
     if (a->B < 0 || a->Tq < 0 || a->cap < 0) return fail(CSA2_E_INVALID, "csa2_index_score: negative size");

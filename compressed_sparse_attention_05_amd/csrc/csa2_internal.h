@@ -14,6 +14,12 @@ namespace csa2 {
 hipError_t launch_kv_write(const void* x, bool x_bf16, int64_t n_rows, int D, const int64_t* dst_row,
                            int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const void* krows,
                            int64_t krow_bytes, void* kcache, hipStream_t st);
+// MXFP4 quantisation plus the indexer-K projection k = bf16(x . W) of the same
+// rows into the tiled bfloat16 indexer cache, in one launch.
+bool kv_project_shape_supported(int D, int d_I);
+hipError_t launch_kv_write_project(const void* x, bool x_bf16, int64_t n_rows, int D, const int64_t* dst_row,
+                                   int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const float* W,
+                                   int d_I, void* kcache, hipStream_t st);
 
 struct ScoreLaunch {
     const void* q_idx; bool q_bf16;

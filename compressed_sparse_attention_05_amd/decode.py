@@ -76,8 +76,12 @@ class DecodeStep:
                  pool: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
                  build_pool: bool = True, mfma_select: bool = False,
                  enc_caches: Optional[List[DecodeCache]] = None, enc_q_pos: Optional[torch.Tensor] = None,
-                 enc_m: int = 2, enc_writes: Optional[List[Optional[tuple]]] = None):
-        """enc_caches: one KV set per E layer, in schedule order.
+                 enc_m: int = 2, enc_writes: Optional[List[Optional[tuple]]] = None,
+                 w_ik: Optional[torch.Tensor] = None):
+        """w_ik: [D][d_I] float32 indexer-K projection weights; when given, the
+        token's indexer key is projected from new_kv in the same launch as its
+        MXFP4 write (csa2_kv_write_project) instead of passed as new_kidx.
+        enc_caches: one KV set per E layer, in schedule order.
         enc_q_pos: [B] int64 absolute position of the token in each sequence
         (E layers' visibility).  enc_writes: per E layer, None or
         (new_kv [B][D], new_kidx [B][d_I], dst_row [B] int64) for an entry
@@ -103,7 +107,18 @@ class DecodeStep:
         self._keep = []          # keep ctypes structs and tensors alive
 
         # ---- write of the new token's entry
-        if new_kv is not None:
+        if new_kv is not None and w_ik is not None:
+            if new_kidx is not None:
+                raise ValueError("pass either new_kidx or w_ik, not both")
+            if w_ik.dtype != torch.float32 or tuple(w_ik.shape) != (D, d_I) or not w_ik.is_contiguous():
+                raise ValueError("w_ik must be a contiguous float32 [D][d_I] tensor")
+            if cache.k_idx.dtype != torch.bfloat16:
+                raise ValueError("projected indexer keys go to a bfloat16 indexer cache")
+            args = (bd._ptr(new_kv), bd._dtype(new_kv, "new_kv"), new_kv.shape[0], D, bd._ptr(dst_row),
+                    B * cap, bd._ptr(cache.codes), bd._ptr(cache.scales), bd._ptr(w_ik), d_I,
+                    bd._ptr(cache.k_idx), None)
+            self.calls.append(("write", self.L.csa2_kv_write_project, args))
+        elif new_kv is not None:
             n_cache_rows = B * cap
             kdt = bd._dtype(new_kidx, "new_kidx") if new_kidx is not None else 0
             args = (bd._ptr(new_kv), bd._dtype(new_kv, "new_kv"), new_kv.shape[0], D, bd._ptr(dst_row),

@@ -135,6 +135,7 @@ TID_K_IDX = 3      # indexer key cache [B][cap][d_I]
 TID_KV = 4         # main KV latent before quantisation [B][cap][D]
 TID_Q = 5          # attention query [B][H][D]
 TID_SWA = 6        # sliding-window KV [B][W][D]
+TID_W_IK = 7       # indexer-K projection weights [D][d_I]
 
 
 def layer_tid(role: int, layer: int) -> int:

@@ -85,6 +85,34 @@ int mxfp4_kv_write(const void *x, int x_dtype, int64_t n_rows, int32_t D,
                    void *stream);
 
 /* ------------------------------------------------------------------------
+ * csa2_kv_write_project - mxfp4_kv_write with the indexer key derived from
+ * the same rows instead of passed in.  A Full layer projects its indexer K
+ * directly from its main KV ([KVC] section 2); the pages give neither the
+ * weights nor the precision, and this library reads the projection as
+ *     acc = +0; for c in 0..D-1: acc = fma(x[c], w_ik[c][j], acc)   (float32)
+ *     k[j] = acc rounded to the nearest bfloat16 (ties to the even mantissa;
+ *            a value past the largest finite bfloat16 stays finite)
+ * over the pre-quantisation latent row x (bf16 inputs widened exactly), so
+ * the indexer keys, and every score and index chosen from them, are
+ * bit-reproducible.  One launch does both jobs.
+ *
+ * x           [n_rows][D] (x_dtype: CSA2_F32 or CSA2_BF16), 16-byte aligned
+ * dst_row     [n_rows] int64 flat destination rows; rows outside
+ *             [0, n_cache_rows) are skipped (codes, scales and key alike)
+ * codes, scales  as mxfp4_kv_write
+ * w_ik        [D][d_I] float32 projection weights, row-major (device)
+ * idx_k_cache bfloat16, TILED layout (see csa2_index_score), n_cache_rows
+ *             rows of d_I; 16-byte aligned
+ * Requires D % 16 == 0, d_I % 8 == 0, n_cache_rows % 64 == 0, and
+ * 64*D + 32*d_I <= 65536 (LDS for a 16-row group; D = 512 allows d_I <= 1024),
+ * else CSA2_E_UNSUPPORTED.  Caller owns every buffer; nothing is allocated.
+ * ------------------------------------------------------------------------ */
+int csa2_kv_write_project(const void *x, int x_dtype, int64_t n_rows, int32_t D,
+                          const int64_t *dst_row, int64_t n_cache_rows, uint8_t *codes,
+                          uint8_t *scales, const float *w_ik, int32_t d_I, void *idx_k_cache,
+                          void *stream);
+
+/* ------------------------------------------------------------------------
  * csa2_index_score - sparse-indexer scores ([KVC] sections 2-3; [DR] 03).
  * The pages give no score formula; this library fixes
  *     s_t = sum_h w_h * ReLU(q_h . k_t)

@@ -152,3 +152,19 @@ def test_decode_select_argument_checks():
     assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 2
     a.q_dtype, a.B = 1, 0
     assert L.csa2_decode_scan(ctypes.byref(a), None, 0, None) == 0  # nothing to do
+
+
+def test_kv_write_project_rejects_bad_arguments_on_host():
+    L = binding.lib()
+    p = ctypes.c_void_p(256)
+    rc = L.csa2_kv_write_project(p, 0, 4, 500, p, 64, p, p, p, 128, p, None)
+    assert rc == 1 and "multiple of 16" in _err()
+    rc = L.csa2_kv_write_project(p, 0, 4, 512, p, 64, p, p, p, 12, p, None)
+    assert rc == 1 and "multiple of 8" in _err()
+    rc = L.csa2_kv_write_project(p, 0, 4, 512, p, 100, p, p, p, 128, p, None)
+    assert rc == 1 and "% 64" in _err()
+    rc = L.csa2_kv_write_project(p, 0, 4, 1024, p, 64, p, p, p, 128, p, None)
+    assert rc == 2 and "LDS" in _err()
+    rc = L.csa2_kv_write_project(p, 0, 4, 512, p, 64, p, p, None, 128, p, None)
+    assert rc == 1 and "null" in _err()
+    assert L.csa2_kv_write_project(None, 0, 0, 512, None, 64, None, None, None, 128, None, None) == 0

@@ -25,11 +25,13 @@ def K():
     return K
 
 
-@pytest.mark.parametrize("k,P_b,mfma", [(256, 512, False), (600, 512, False), (256, 512, True)])
-def test_decode_step_full_reindex_reuse(K, k, P_b, mfma):
+@pytest.mark.parametrize("k,P_b,mfma,project", [(256, 512, False, False), (600, 512, False, False),
+                                                (256, 512, True, False), (256, 512, False, True)])
+def test_decode_step_full_reindex_reuse(K, k, P_b, mfma, project):
     # k <= P_b: the Full layer's pool and top-k run as one launch (or, with
     # mfma, the matrix-core scan and the band-exact selection);
-    # k > P_b: pool, then the Full top-k over the whole row
+    # k > P_b: pool, then the Full top-k over the whole row.  With project,
+    # the token's indexer key is projected from its latent row by the write.
     from compressed_sparse_attention_05_amd.decode import DecodeCache, DecodeStep, LayerInputs
     dev = torch.device("cuda:0")
     B, cap, D, H, d_I, H_I, W = 2, 20032, 512, 64, 128, 8, 128
@@ -52,6 +54,12 @@ def test_decode_step_full_reindex_reuse(K, k, P_b, mfma):
     cache = DecodeCache(codes=codes, scales=scales, k_idx=kcache,
                         ctx_len=torch.tensor(ctx, dtype=torch.int32, device=dev),
                         swa_len=torch.tensor(swa_len, dtype=torch.int32, device=dev))
+    w_ik = None
+    if project:
+        w_ik = ci.gaussian(seed, ci.TID_W_IK, (D, d_I)) * np.float32(1.0 / math.sqrt(D))
+        for b in range(B):
+            bits = oracle.project_kidx(kv[b, ctx[b] - 1:ctx[b]], w_ik)
+            kidx[b, ctx[b] - 1] = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16)[0]
     layers = []
     for li in range(3):
         q = ci.gaussian(seed + li, ci.TID_Q, (B, H, D), dtype=torch.bfloat16)
@@ -62,8 +70,9 @@ def test_decode_step_full_reindex_reuse(K, k, P_b, mfma):
     lin = [LayerInputs(q=q.to(dev), swa=swa.to(dev), q_idx=qi.to(dev), w=wi.to(dev)) for q, swa, qi, wi in layers]
     step = DecodeStep("FXR", cache, lin, k=k, P_b=P_b,
                       new_kv=flat_kv[new_rows.to(dev)].contiguous(),
-                      new_kidx=kidx.reshape(B * cap, d_I)[new_rows].contiguous().to(dev),
-                      dst_row=new_rows.to(dev), mfma_select=mfma)
+                      new_kidx=None if project else kidx.reshape(B * cap, d_I)[new_rows].contiguous().to(dev),
+                      dst_row=new_rows.to(dev), mfma_select=mfma,
+                      w_ik=w_ik.to(dev) if project else None)
     step.run()
     torch.cuda.synchronize()
     sm = 1.0 / math.sqrt(D)
