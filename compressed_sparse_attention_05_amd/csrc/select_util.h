@@ -293,7 +293,13 @@ __device__ __forceinline__ uint32_t sel_stats(const uint32_t (&kk)[R], SelLds& s
 // Stage 2: the exact need-th largest key T (need >= 1 nonempty keys exist)
 // and, on return, need = how many keys equal to T belong to the selection.
 // hist[0] must be clear (sel_stats); both histograms are left dirty.
-template <int R>
+// EARLY: stop as soon as the digit's bin holds exactly the keys still needed
+// (then every key in it is chosen); the result is then one below the
+// smallest key the resolved prefix allows, with need = 0, so "key > result"
+// is exactly the selection.  Random scores reach that after two passes
+// instead of running down to bit 0.  Without EARLY the result is the exact
+// need-th key.
+template <int R, bool EARLY = false>
 __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t mn, uint32_t mx, uint32_t& need,
                                                SelLds& sh) {
     if (mn == mx) return mn;                       // every nonempty key is T
@@ -360,12 +366,15 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
         }
         const uint32_t excl = acc + incl - s8;
         const bool mine = excl < need && excl + s8 >= need;
-        uint32_t digit = 0, above = 0;
+        uint32_t digit = 0, above = 0, in_bin = 0;
         if (mine) {
             uint32_t a = excl;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                if (a + c[i] >= need) { digit = static_cast<uint32_t>(hbw + 7 - i); above = a; break; }
+                if (a + c[i] >= need) {
+                    digit = static_cast<uint32_t>(hbw + 7 - i); above = a; in_bin = c[i];
+                    break;
+                }
                 a += c[i];
             }
         }
@@ -375,6 +384,14 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
         above = __shfl(above, src);
         known = (known << nb) | digit;
         need -= above;
+        if (EARLY && shift > 0) {
+            in_bin = __shfl(in_bin, src);
+            const uint32_t lowest = static_cast<uint32_t>(known) << shift;
+            if (in_bin == need && lowest != 0u) {
+                need = 0;
+                return lowest - 1u;
+            }
+        }
         top = shift - 1;
         buf ^= 1;
     }
@@ -384,15 +401,19 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
 // Choose the k best keys of the workgroup's slots (thread t: slots
 // [tR, tR + R) in kk, 0 = empty) and call out(rank, j) for each chosen slot
 // tR + j in ascending slot order.  Returns min(k, #nonempty).
+// If lb is given, *lb is set to a key no larger than any chosen key (every
+// chosen key is >= *lb; 0 when nothing is chosen).
 template <int R, class Out>
-__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out) {
+__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out, uint32_t* lb = nullptr) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     uint32_t mn, mx;
     const uint32_t n_valid = sel_stats<R>(kk, sh, mn, mx);
     const uint32_t k_eff = n_valid < k ? n_valid : k;
+    if (lb) *lb = 0u;
     if (k_eff == 0) return 0;
     uint32_t need = k_eff;
-    const uint32_t T = sel_passes<R>(kk, mn, mx, need, sh);
+    const uint32_t T = sel_passes<R, true>(kk, mn, mx, need, sh);
+    if (lb) *lb = need == 0 ? T + 1u : T;
 
     // ---- 3. ordered emission: one scan of (above << 16 | ties)
     uint32_t above = 0, ties = 0;

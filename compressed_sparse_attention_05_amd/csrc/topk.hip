@@ -382,16 +382,18 @@ __global__ __launch_bounds__(kThreads) void pool_topk_kernel(const float* __rest
     __shared__ SelLds sh;
     __shared__ int32_t pool_s[kPoolMax];
     const int64_t row = blockIdx.x;
+    uint32_t got_pool = 0, pool_lb = 0;
     {
         const float* bm = bmax + row * ld_bm;
         int32_t* po = pool + row * static_cast<int64_t>(P_b);
         const int64_t r0 = static_cast<int64_t>(threadIdx.x) * R1;
         uint32_t kk[R1];
         load_run_keys<R1>(bm, r0, n_blocks, kk);
-        const uint32_t got = select_run<R1>(kk, static_cast<uint32_t>(P_b), sh, [&](uint32_t r, int j) {
+        got_pool = select_run<R1>(kk, static_cast<uint32_t>(P_b), sh, [&](uint32_t r, int j) {
             po[r] = static_cast<int32_t>(r0) + j;
             pool_s[r] = static_cast<int32_t>(r0) + j;
-        });
+        }, &pool_lb);
+        const uint32_t got = got_pool;
         for (int i = static_cast<int>(got) + threadIdx.x; i < P_b; i += kThreads) {
             po[i] = -1;
             pool_s[i] = -1;
@@ -422,6 +424,14 @@ __global__ __launch_bounds__(kThreads) void pool_topk_kernel(const float* __rest
             for (int e = 0; e < 8; ++e)
                 kk[8 * q + e] = (blk[q] >= 0 && p0 + e < ld) ? key_of(s[p0 + e]) : 0u;
         }
+    }
+    // Every chosen block's maximum is >= pool_lb, so with a full pool of P_b
+    // >= k blocks at least k pool scores are >= pool_lb and the k-th best
+    // score is too: scores below it cannot be chosen and leave the
+    // selection as empty slots, which keeps them out of its histograms.
+    if (got_pool == static_cast<uint32_t>(P_b) && pool_lb != 0u) {
+#pragma unroll
+        for (int e = 0; e < R2; ++e) kk[e] = kk[e] >= pool_lb ? kk[e] : 0u;
     }
     const uint32_t got = select_run<R2>(kk, static_cast<uint32_t>(k), sh, [&](uint32_t r, int j) {
         o[r] = blk[j >> 3] * 8 + (j & 7);
