@@ -384,6 +384,48 @@ def run_project(K, dev, reps: int = 50):
     return res
 
 
+def run_mhc(K, dev, reps: int = 20, T: int = 8192, d: int = 4096):
+    """Single-pass mHC step (n = 4 streams of d = 4,096 channels, bfloat16)
+    for the 8,192 tokens of a prefill chunk.  Algorithmic bytes per launch:
+    (2n + 2) * d * 2 per token (read X and f, write X_next and u) plus the
+    coefficients in and out and the projection weights once."""
+    n, K_out = 4, 24
+    sets = []
+    for i in range(2):
+        seed = 900 + i
+        X = ci.gaussian(seed, ci.TID_MHC_X, (T, n, d), dtype=torch.bfloat16, device=dev)
+        f = ci.gaussian(seed, ci.TID_MHC_F, (T, d), dtype=torch.bfloat16, device=dev)
+        coef = ci.uniform(seed, ci.TID_MHC_COEF, (T, n + n * n + n), device=dev)
+        A = (0.1 + 0.9 * coef[:, :n]).contiguous()
+        B = (0.5 * coef[:, n:n + n * n]).reshape(T, n, n).contiguous()
+        C = (0.2 + 1.6 * coef[:, n + n * n:]).contiguous()
+        phiT = (ci.gaussian(seed, ci.TID_MHC_PHI, (K_out, n * d), device=dev) / math.sqrt(n * d)).to(torch.bfloat16)
+        bias = 0.5 * ci.gaussian(seed + 1, ci.TID_MHC_PHI, (K_out,), device=dev)
+        out = (torch.empty_like(X), torch.empty_like(f), torch.empty_like(A), torch.empty_like(B),
+               torch.empty_like(C))
+        sets.append((X, f, A, B, C, phiT, bias, out))
+
+    def call(s):
+        X, f, A, B, C, phiT, bias, out = s
+        K.csa2_mhc_step(X, f, A, B, C, phiT, bias, (1.0, 1.0, 1.0), iters=20, out=out)
+
+    for i in range(4):
+        call(sets[i % 2])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        call(sets[i % 2])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    alg = T * ((2 * n + 2) * d * 2 + 2 * (n + n * n + n) * 4) + K_out * n * d * 2
+    return {"workload": f"mhc-step-t{T}-n{n}-d{d}", "tokens": T, "streams": n, "channels": d,
+            "us_per_step": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
+            "algorithmic_bytes": alg, "GBps": round(alg / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
     """The oracle, as it stands, on n_queries sequences of the workload's
     first Full layer (write + scan + block max + pool + top-k + attention).
@@ -467,6 +509,8 @@ def main(argv=None):
                     help="only time the decoder replay workload (profiling)")
     ap.add_argument("--project-only", action="store_true",
                     help="only time the write with the projected indexer key (profiling)")
+    ap.add_argument("--mhc-only", action="store_true",
+                    help="only time the single-pass mHC step (profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
@@ -495,6 +539,9 @@ def main(argv=None):
         return 0
     if args.project_only:
         print(json.dumps(run_project(K, dev)), flush=True)
+        return 0
+    if args.mhc_only:
+        print(json.dumps(run_mhc(K, dev)), flush=True)
         return 0
     w = ci.WORKLOADS[args.workload]
     if "F" not in w.schedule:
@@ -583,6 +630,8 @@ def main(argv=None):
         print(f"# setting up {ci.DECODER_REPLAY.name}", file=sys.stderr, flush=True)
         sec.append(run_replay(K, ci.DECODER_REPLAY, 3, 1, dev))
         sec.append(run_project(K, dev))
+        torch.cuda.empty_cache()
+        sec.append(run_mhc(K, dev))
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
     return 0

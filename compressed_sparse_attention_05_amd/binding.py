@@ -30,6 +30,13 @@ class ScoreArgs(ctypes.Structure):
                 ("scores", P), ("ld_scores", i64), ("block_max", P)]
 
 
+class MhcArgs(ctypes.Structure):
+    _fields_ = [("X", P), ("f", P), ("A", P), ("B", P), ("C", P), ("phiT", P), ("bias", P),
+                ("alpha_pre", ctypes.c_float), ("alpha_post", ctypes.c_float), ("alpha_res", ctypes.c_float),
+                ("T", i64), ("n", i32), ("d", i32), ("iters", i32),
+                ("X_next", P), ("u_next", P), ("A_next", P), ("B_next", P), ("C_next", P)]
+
+
 class AttnArgs(ctypes.Structure):
     _fields_ = [("q", P), ("q_dtype", i32), ("codes", P), ("scales", P), ("cap", i64),
                 ("idx", P), ("k", i32), ("swa", P), ("swa_dtype", i32), ("W", i32),
@@ -62,6 +69,7 @@ SIGNATURES = {
     "csa2_last_error": (ctypes.c_char_p, []),
     "mxfp4_kv_write": (ctypes.c_int, [P, ctypes.c_int, i64, i32, P, i64, P, P, P, ctypes.c_int, i32, P, P]),
     "csa2_kv_write_project": (ctypes.c_int, [P, ctypes.c_int, i64, i32, P, i64, P, P, P, i32, P, P]),
+    "csa2_mhc_step": (ctypes.c_int, [ctypes.POINTER(MhcArgs), P]),
     "csa2_index_score_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScoreArgs)]),
     "csa2_index_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, ctypes.c_size_t, P]),
     "csa2_topk_workspace_size": (ctypes.c_size_t, [i64, i64, i32]),
@@ -213,6 +221,38 @@ def csa2_kv_write_project(x, dst_row, codes, scales, w_ik, idx_k_cache, stream=N
     _check(lib().csa2_kv_write_project(_ptr(x), _dtype(x, "x"), n, D, _ptr(dst_row), n_cache_rows,
                                        _ptr(codes), _ptr(scales), _ptr(w_ik), d_I, _ptr(idx_k_cache),
                                        _stream(stream)))
+
+
+def csa2_mhc_step(X, f, A, B, C, phiT, bias, alphas, iters: int = 20, out=None, stream=None):
+    """One fused single-pass mHC step for T tokens.  X [T][n][d] bf16, f [T][d]
+    bf16, A [T][n], B [T][n][n], C [T][n] f32, phiT [2n+n^2][n*d] bf16, bias
+    [2n+n^2] f32, alphas = (alpha_pre, alpha_post, alpha_res).  Returns
+    (X_next, u_next, A_next, B_next, C_next); `out` may supply them."""
+    for t, nm in ((X, "X"), (f, "f"), (A, "A"), (B, "B"), (C, "C"), (phiT, "phiT"), (bias, "bias")):
+        _dev(t, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if X.dtype != torch.bfloat16 or f.dtype != torch.bfloat16 or phiT.dtype != torch.bfloat16:
+        raise TypeError("X, f and phiT must be bfloat16")
+    for t, nm in ((A, "A"), (B, "B"), (C, "C"), (bias, "bias")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    T, n, d = X.shape
+    K = 2 * n + n * n
+    if (tuple(f.shape) != (T, d) or tuple(A.shape) != (T, n) or tuple(B.shape) != (T, n, n)
+            or tuple(C.shape) != (T, n) or tuple(phiT.shape) != (K, n * d) or tuple(bias.shape) != (K,)):
+        raise ValueError("mHC argument shapes do not match X [T][n][d]")
+    if out is None:
+        out = (torch.empty_like(X), torch.empty_like(f), torch.empty_like(A), torch.empty_like(B),
+               torch.empty_like(C))
+    Xn, u, An, Bn, Cn = out
+    a = MhcArgs(X=X.data_ptr(), f=f.data_ptr(), A=A.data_ptr(), B=B.data_ptr(), C=C.data_ptr(),
+                phiT=phiT.data_ptr(), bias=bias.data_ptr(), alpha_pre=float(alphas[0]),
+                alpha_post=float(alphas[1]), alpha_res=float(alphas[2]), T=T, n=n, d=d, iters=iters,
+                X_next=Xn.data_ptr(), u_next=u.data_ptr(), A_next=An.data_ptr(), B_next=Bn.data_ptr(),
+                C_next=Cn.data_ptr())
+    _check(lib().csa2_mhc_step(ctypes.byref(a), _stream(stream)))
+    return out
 
 
 def csa2_index_score(q_idx, w, k_idx, ctx_len, *, q_pos=None, m: int = 1, pool_blocks=None,

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
 SOURCES = ["csa2_api.hip", "kv_write.hip", "score.hip", "topk.hip", "attn.hip", "prefill_topk.hip",
-           "decode_select.hip"]
+           "decode_select.hip", "mhc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -405,4 +405,31 @@ int csa2_prefill_topk(const csa2_prefill_topk_args* a, void* ws, size_t ws_bytes
     return device_status(csa2::launch_prefill_topk(L, ws, as_stream(stream)), "csa2_prefill_topk");
 }
 
+// --------------------------------------------------------------------------
+int csa2_mhc_step(const csa2_mhc_args* m, void* stream) {
+    if (!m) return fail(CSA2_E_INVALID, "csa2_mhc_step: args is null");
+    if (m->T < 0) return fail(CSA2_E_INVALID, "csa2_mhc_step: T < 0");
+    if (m->n <= 0 || m->d <= 0) return fail(CSA2_E_INVALID, "csa2_mhc_step: n and d must be positive");
+    if (m->iters < 0) return fail(CSA2_E_INVALID, "csa2_mhc_step: iters < 0");
+    if (!csa2::mhc_shape_supported(m->n, m->d))
+        return fail(CSA2_E_UNSUPPORTED, "csa2_mhc_step: (n=%d, d=%d) not supported (n = 4, d a multiple of 256)",
+                    m->n, m->d);
+    if (m->T == 0) return ok();
+    if (!m->X || !m->f || !m->A || !m->B || !m->C || !m->phiT || !m->bias || !m->X_next || !m->u_next ||
+        !m->A_next || !m->B_next || !m->C_next)
+        return fail(CSA2_E_INVALID, "csa2_mhc_step: null pointer");
+    if (!aligned(m->X, 16) || !aligned(m->f, 16) || !aligned(m->phiT, 16) || !aligned(m->X_next, 16) ||
+        !aligned(m->u_next, 16))
+        return fail(CSA2_E_INVALID, "csa2_mhc_step: X, f, phiT, X_next and u_next must be 16-byte aligned");
+    csa2::MhcLaunch p;
+    p.X = static_cast<const uint16_t*>(m->X); p.f = static_cast<const uint16_t*>(m->f);
+    p.A = m->A; p.B = m->B; p.C = m->C;
+    p.phiT = static_cast<const uint16_t*>(m->phiT); p.bias = m->bias;
+    p.alpha_pre = m->alpha_pre; p.alpha_post = m->alpha_post; p.alpha_res = m->alpha_res;
+    p.T = m->T; p.d = m->d; p.iters = m->iters;
+    p.Xn = static_cast<uint16_t*>(m->X_next); p.u = static_cast<uint16_t*>(m->u_next);
+    p.An = m->A_next; p.Bn = m->B_next; p.Cn = m->C_next;
+    return device_status(csa2::launch_mhc_step(p, as_stream(stream)), "csa2_mhc_step");
+}
+
 }  // extern "C"

@@ -101,4 +101,17 @@ size_t decode_select_workspace_bytes(int64_t B, int64_t cap);
 hipError_t launch_decode_scan(const DecodeSelectLaunch& L, void* ws, hipStream_t st);
 hipError_t launch_decode_select(const DecodeSelectLaunch& L, void* ws, hipStream_t st);
 
+// ---- single-pass mHC block step (n = 4 streams, bfloat16 storage)
+struct MhcLaunch {
+    const uint16_t* X; const uint16_t* f;        // [T][4][d], [T][d] bf16
+    const float* A; const float* B; const float* C;  // [T][4], [T][4][4], [T][4]
+    const uint16_t* phiT; const float* bias;     // [24][4d] bf16, [24]
+    float alpha_pre, alpha_post, alpha_res;
+    int64_t T; int d; int iters;
+    uint16_t* Xn; uint16_t* u;                   // [T][4][d], [T][d] bf16
+    float* An; float* Bn; float* Cn;             // [T][4], [T][4][4], [T][4]
+};
+bool mhc_shape_supported(int n, int d);
+hipError_t launch_mhc_step(const MhcLaunch& p, hipStream_t st);
+
 }  // namespace csa2

@@ -136,6 +136,10 @@ TID_KV = 4         # main KV latent before quantisation [B][cap][D]
 TID_Q = 5          # attention query [B][H][D]
 TID_SWA = 6        # sliding-window KV [B][W][D]
 TID_W_IK = 7       # indexer-K projection weights [D][d_I]
+TID_MHC_X = 8      # mHC residual streams [T][n][d]
+TID_MHC_F = 9      # mHC block output [T][d]
+TID_MHC_COEF = 10  # mHC incoming coefficients A, B, C
+TID_MHC_PHI = 11   # mHC projection phiT [2n+n^2][n*d] and bias
 
 
 def layer_tid(role: int, layer: int) -> int:

@@ -366,6 +366,60 @@ size_t csa2_decode_select_workspace_size(const csa2_decode_select_args *a);
 int csa2_decode_scan(const csa2_decode_select_args *a, void *ws, size_t ws_bytes, void *stream);
 int csa2_decode_select(const csa2_decode_select_args *a, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * csa2_mhc_step - one fused pass of single-pass mHC ([KVC] section 6; [SUM]
+ * Methodology item 4, equation (6)).  The residual stream of a token is n
+ * streams X_l [n][d]; the pages shift the input-mixing coefficient by one
+ * block,
+ *     X_{l+1} = B_l X_l + C_l F_l(A_{l-1} X_l),  (A_l, B_l, C_l) = H(X_l),
+ * so that one read of X_l serves the residual update, the next block's input
+ * mixing and the statistics of H.  Per token this call computes, from X_l,
+ * the block output f_l = F_l(A_{l-1} X_l) and the coefficients (A_l, B_l, C_l)
+ * of the previous pass:
+ *     X_next = bf16(B_l X_l + C_l f_l)            (float32, rounded once)
+ *     u_next = bf16(A_l X_next)                   (input of F_{l+1})
+ *     (A_next, B_next, C_next) = H(X_next)
+ * reading (n + 1) d and writing (n + 1) d bfloat16 values: the (2n+2)d bound.
+ * H is not defined on the pages; this library reads it as the manifold-
+ * constrained hyper-connection form over x = X_next flattened stream-major
+ * (index i*d + c):
+ *     r = sqrt(mean(x^2) + 1e-6),   z = (phiT . x) / r   (z has 2n + n^2 entries)
+ *     A_next = sigmoid(alpha_pre * z[0:n] + bias[0:n])
+ *     C_next = 2 * sigmoid(alpha_post * z[n:2n] + bias[n:2n])
+ *     B_next = Sinkhorn_iters(exp(alpha_res * z[2n:] + bias[2n:]) as n x n,
+ *              row-major), each round dividing every row by its sum, then
+ *              every column by its sum.
+ * The projection runs on the matrix cores in float32 accumulation and the
+ * epilogue in float32, so A/B/C_next are not bit-reproducible across
+ * implementations; X_next is within one bfloat16 ulp of the exactly rounded
+ * value.
+ *
+ * Layouts (row-major, device pointers, caller-owned; nothing is allocated):
+ *   X, X_next [T][n][d] bf16;  f, u_next [T][d] bf16;  phiT [2n+n^2][n*d] bf16;
+ *   A, A_next, C, C_next [T][n] f32;  B, B_next [T][n][n] f32;  bias [2n+n^2] f32.
+ * Supported: n = 4, d a multiple of 256 (else CSA2_E_UNSUPPORTED).  X, f, phiT,
+ * X_next and u_next must be 16-byte aligned.  X_next must not alias X.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_mhc_args {
+    const void *X;       /* [T][n][d] bf16 */
+    const void *f;       /* [T][d] bf16 */
+    const float *A;      /* [T][n] */
+    const float *B;      /* [T][n][n] */
+    const float *C;      /* [T][n] */
+    const void *phiT;    /* [2n+n^2][n*d] bf16 */
+    const float *bias;   /* [2n+n^2] */
+    float alpha_pre, alpha_post, alpha_res;
+    int64_t T;
+    int32_t n, d, iters;
+    void *X_next;        /* [T][n][d] bf16 */
+    void *u_next;        /* [T][d] bf16 */
+    float *A_next;       /* [T][n] */
+    float *B_next;       /* [T][n][n] */
+    float *C_next;       /* [T][n] */
+} csa2_mhc_args;
+
+int csa2_mhc_step(const csa2_mhc_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
