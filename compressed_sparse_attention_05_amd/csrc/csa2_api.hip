@@ -412,7 +412,7 @@ int csa2_mhc_step(const csa2_mhc_args* m, void* stream) {
     if (m->n <= 0 || m->d <= 0) return fail(CSA2_E_INVALID, "csa2_mhc_step: n and d must be positive");
     if (m->iters < 0) return fail(CSA2_E_INVALID, "csa2_mhc_step: iters < 0");
     if (!csa2::mhc_shape_supported(m->n, m->d))
-        return fail(CSA2_E_UNSUPPORTED, "csa2_mhc_step: (n=%d, d=%d) not supported (n = 4, d a multiple of 256)",
+        return fail(CSA2_E_UNSUPPORTED, "csa2_mhc_step: (n=%d, d=%d) not supported (n = 4, d a multiple of 128)",
                     m->n, m->d);
     if (m->T == 0) return ok();
     if (!m->X || !m->f || !m->A || !m->B || !m->C || !m->phiT || !m->bias || !m->X_next || !m->u_next ||

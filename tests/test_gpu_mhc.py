@@ -89,7 +89,7 @@ def check(inp, got, alphas, iters, rows=None):
         assert err <= 1e-3, (nm, err)
 
 
-@pytest.mark.parametrize("T,d,seed", [(100, 512, 61), (1, 256, 62), (64, 4096, 63)])
+@pytest.mark.parametrize("T,d,seed", [(100, 512, 61), (1, 256, 62), (64, 4096, 63), (33, 384, 66), (5, 128, 67)])
 def test_mhc_step_matches_oracle(K, T, d, seed):
     print(f"mhc T={T} d={d} seed={seed}", flush=True)
     inp = make_inputs(seed, T, d)
