@@ -917,38 +917,61 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     }
 }
 
-// Merge the key-split partials of one (unit, 64-head block): workgroup y
-// covers one (wave, row-tile) block of the partial layout, i.e. 32 heads x
-// 32 consecutive channels.  Reads are in the partials' own (coalesced)
-// order; the result is transposed through LDS so the output rows are
-// written as 128-byte runs.
+// Merge the key-split partials of one (unit, 64-head block).  A block of
+// the partial layout is one (wave, row-tile) pair: 32 heads (head group hg =
+// wave & 1) x 32 consecutive channels.  Workgroup (ub, hg, g) merges `bpw`
+// consecutive blocks of head group hg, so the per-head split weights are
+// formed once for all of them; with many units bpw = 4 cuts the number of
+// workgroups (each pays a fixed chain of dependent loads and barriers) by 4.
+// Reads are in the partials' own (coalesced) order; each result block is
+// transposed through LDS so the output rows are written as 128-byte runs.
 template <int D, int NQ>
 __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ ws_o,
                                                        const float* __restrict__ ws_m,
                                                        const float* __restrict__ ws_l, int splits,
-                                                       int H, int hblocks, float* __restrict__ out) {
+                                                       int H, int hblocks, int bpw, float* __restrict__ out) {
     constexpr int DQ = D / NQ, MT = DQ / 32;
     __shared__ float tile[32][33];
     __shared__ float wgt[kCombineMaxSplits][32];   // m_s, then exp2(m_s - m*), per split and head
     __shared__ float lsum[kCombineMaxSplits][32];
     __shared__ float inv_den[32];
     const int64_t ub = blockIdx.x;                 // unit * hblocks + hb
-    const int wv = blockIdx.y / MT, mt = blockIdx.y % MT;
-    const int hg = wv & 1, dqq = wv >> 1;
+    const int hg = blockIdx.y;
     const int t = threadIdx.x, r = t >> 6, ln = t & 63;
     const int hcol = ln & 31;
     const int dd = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-    const int64_t nat = ((wv * MT + mt) * 16 + r) * 64 + ln;
-    const float* po = ws_o + ub * splits * static_cast<int64_t>(64 * D) + nat;
     constexpr int64_t PS = 64 * D;                 // partial stride
-    // the first 16 splits' partials are loaded before the weights are
-    // formed, so the two latencies overlap
+    const float* pbase = ws_o + ub * splits * static_cast<int64_t>(64 * D);
+    const int hb = static_cast<int>(ub % hblocks);
+    const int64_t u = ub / hblocks;
+    const int oh = t >> 5, od = t & 31;
+    const int head = hb * 64 + 32 * hg + oh;
+    // block j of head group hg: dqq = j / MT, mt = j % MT, wave 2 dqq + hg
+    auto block_ptr = [&](int j) {
+        const int wv = 2 * (j / MT) + hg, mt = j % MT;
+        return pbase + ((wv * MT + mt) * 16 + r) * 64 + ln;
+    };
+    const int j0 = blockIdx.z * bpw;
+    // Loads are issued before the weights are formed, so the two latencies
+    // overlap: with 4 blocks of at most 4 splits (many units), all 16 of
+    // them; otherwise the first block's first 16 splits.
+    const bool all16 = bpw == 4 && splits <= 4;
     constexpr int kEarly = 16;
     float oe[kEarly];
+    if (all16) {
 #pragma unroll
-    for (int i = 0; i < kEarly; ++i) oe[i] = i < splits ? po[i * PS] : 0.0f;
-    // per-head split weights, once per block: thread t loads (split t/32,
-    // head 32hg + t%32), then thread t < 32 reduces over the splits in LDS
+        for (int jj = 0; jj < 4; ++jj) {
+            const float* po = block_ptr(j0 + jj);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) oe[4 * jj + s] = s < splits ? po[s * PS] : 0.0f;
+        }
+    } else {
+        const float* po = block_ptr(j0);
+#pragma unroll
+        for (int i = 0; i < kEarly; ++i) oe[i] = i < splits ? po[i * PS] : 0.0f;
+    }
+    // per-head split weights, once per workgroup: thread t loads (split
+    // t/32, head 32hg + t%32), then thread t < 32 reduces over the splits
     {
         const int h = t & 31;
         for (int s = t >> 5; s < splits; s += 32) {
@@ -971,25 +994,43 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
         inv_den[t] = den > 0.0f ? 1.0f / den : 0.0f;
     }
     __syncthreads();
-    float num = 0.0f;
+    auto emit = [&](int j, float num, bool first) {
+        if (!first) __syncthreads();               // the previous block's tile has been written out
+        tile[hcol][dd] = num * inv_den[hcol];
+        __syncthreads();
+        const int dqq = j / MT, mt = j % MT;
+        if (head < H) out[(u * H + head) * D + dqq * DQ + 32 * mt + od] = tile[oh][od];
+    };
+    if (all16) {
 #pragma unroll
-    for (int i = 0; i < kEarly; ++i) num += i < splits ? wgt[i][hcol] * oe[i] : 0.0f;
-    int s = kEarly;
-    for (; s + 8 <= splits; s += 8) {
-        float o[8];
+        for (int jj = 0; jj < 4; ++jj) {
+            float num = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = po[(s + i) * PS];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) num += wgt[s + i][hcol] * o[i];
+            for (int s = 0; s < 4; ++s) num += s < splits ? wgt[s][hcol] * oe[4 * jj + s] : 0.0f;
+            emit(j0 + jj, num, jj == 0);
+        }
+        return;
     }
-    for (; s < splits; ++s) num += wgt[s][hcol] * po[s * PS];
-    tile[hcol][dd] = num * inv_den[hcol];
-    __syncthreads();
-    const int hb = static_cast<int>(ub % hblocks);
-    const int64_t u = ub / hblocks;
-    const int oh = t >> 5, od = t & 31;
-    const int head = hb * 64 + 32 * hg + oh;
-    if (head < H) out[(u * H + head) * D + dqq * DQ + 32 * mt + od] = tile[oh][od];
+    for (int jj = 0; jj < bpw; ++jj) {
+        const int j = j0 + jj;
+        const float* po = block_ptr(j);
+        float num = 0.0f;
+        int s = 0;
+        if (jj == 0) {
+#pragma unroll
+            for (int i = 0; i < kEarly; ++i) num += i < splits ? wgt[i][hcol] * oe[i] : 0.0f;
+            s = kEarly;
+        }
+        for (; s + 8 <= splits; s += 8) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = po[(s + i) * PS];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) num += wgt[s + i][hcol] * o[i];
+        }
+        for (; s < splits; ++s) num += wgt[s][hcol] * po[s * PS];
+        emit(j, num, jj == 0);
+    }
 }
 
 struct SplitPlan { int splits, tiles_per_split, n_tiles; };
@@ -1078,8 +1119,12 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
         attn_kernel<D, NQ, BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 128 * NQ, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sp.splits == 1) return e;
-    combine_kernel<D, NQ><<<dim3(static_cast<unsigned>(L.units * hblocks), 2 * NQ * (D / NQ / 32)), 1024, 0, st>>>(
-        a.ws_o, a.ws_m, a.ws_l, sp.splits, L.H, hblocks, L.out);
+    // blocks of one head group: NQ channel slices x (D / NQ / 32) row tiles
+    constexpr int kGroupBlocks = NQ * (D / NQ / 32);
+    const int64_t n_blocks = L.units * hblocks * 2 * kGroupBlocks;
+    const int bpw = (n_blocks >= 4 * kCUs && kGroupBlocks % 4 == 0) ? 4 : 1;
+    combine_kernel<D, NQ><<<dim3(static_cast<unsigned>(L.units * hblocks), 2, kGroupBlocks / bpw), 1024, 0, st>>>(
+        a.ws_o, a.ws_m, a.ws_l, sp.splits, L.H, hblocks, bpw, L.out);
     return hipGetLastError();
 }
 
