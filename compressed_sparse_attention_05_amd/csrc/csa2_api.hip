@@ -89,12 +89,13 @@ int csa2_kv_write_project(const void* x, int x_dtype, int64_t n_rows, int32_t D,
     if (n_cache_rows < 0 || n_cache_rows % 64 != 0)
         return fail(CSA2_E_INVALID, "csa2_kv_write_project: the tiled indexer cache needs n_cache_rows %% 64 == 0");
     if (!csa2::kv_project_shape_supported(D, d_I))
-        return fail(CSA2_E_UNSUPPORTED, "csa2_kv_write_project: (D=%d, d_I=%d) needs more than 64 KiB of LDS", D, d_I);
+        return fail(CSA2_E_UNSUPPORTED, "csa2_kv_write_project: D=%d not supported (D <= 512)", D);
     if (n_rows == 0) return ok();
     if (!x || !dst_row || !codes || !scales || !w_ik || !idx_k_cache)
         return fail(CSA2_E_INVALID, "csa2_kv_write_project: null pointer");
-    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(idx_k_cache, 16))
-        return fail(CSA2_E_INVALID, "csa2_kv_write_project: x and idx_k_cache must be 16-byte and codes 8-byte aligned");
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(idx_k_cache, 16) || !aligned(w_ik, 16))
+        return fail(CSA2_E_INVALID,
+                    "csa2_kv_write_project: x, w_ik and idx_k_cache must be 16-byte and codes 8-byte aligned");
     hipError_t e = csa2::launch_kv_write_project(x, x_dtype == CSA2_BF16, n_rows, D, dst_row, n_cache_rows, codes,
                                                  scales, w_ik, d_I, idx_k_cache, as_stream(stream));
     return device_status(e, "csa2_kv_write_project");

@@ -131,18 +131,20 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 // weights W[D][d_I], each output an fma chain over the channels in order,
 // rounded to the nearest bfloat16 (ties to even, never to infinity):
 //     acc = +0; for c in 0..D-1: acc = fma(x[c], W[c][j], acc)
-// A workgroup takes 2*RPT rows: their latent rows sit in LDS as float32, and
-// each thread runs the chains of one column j for RPT rows (broadcast LDS
-// reads of x; one coalesced read of W[c][j] per channel serves RPT fmas).  The
-// weights stream through a ring of PF_BLOCKS register blocks of 16 channels,
-// so 64 channels of loads are in flight while a block is consumed.  RPT = 1
-// for a decode token's few rows (many workgroups, short critical path), 8 for
-// a prefill chunk's thousands.  The bfloat16 results are restaged in LDS so
+// Each output is a chain of D dependent fmas, so the design keeps every
+// chain's operands in LDS and gives every thread exactly one chain: a
+// workgroup of 32 ROWS threads owns ROWS rows x a slice of 32 output columns
+// (ROWS = 8 for a decode batch, so its few rows still spread over many
+// workgroups; 32 for a prefill chunk's entries, so each staged weight slice
+// serves more rows).  It stages the latent rows (float32) and the weight
+// slice, transposed to
+// [column][channel] (rows padded by 16 bytes against bank conflicts), with
+// whole-workgroup coalesced loads, then thread (r, j) runs its chain with two
+// 16-byte LDS reads per four fmas.  The bfloat16 keys are restaged in LDS so
 // every store is a whole 16-byte chunk of the tiled indexer cache.
-constexpr int PROJ_THREADS = 256;
-constexpr int PROJ_CB = 16;       // channels per register block
-constexpr int PROJ_PF = 4;        // blocks in flight
-constexpr int PROJ_MAX_RPT = 8;
+constexpr int PROJ_COLS = 32;
+constexpr int PROJ_DMAX = 512;
+constexpr int PROJ_QTHREADS = 256;     // quantising workgroups use their first 256 threads
 
 // bfloat16 nearest to a finite float (ties to the even mantissa).  A float
 // past the largest bfloat16 by at least half an ulp stays at the largest
@@ -153,93 +155,94 @@ __device__ __forceinline__ uint16_t bf16_nearest_finite(float f) {
     return ((r & 0x7f80u) == 0x7f80u) ? static_cast<uint16_t>(u >> 16) : static_cast<uint16_t>(r);
 }
 
-__device__ __forceinline__ void load_wblock(float (&w)[PROJ_CB], const float* __restrict__ W, int c, int D,
-                                            int d_I, int j) {
-    if (c < D) {
-#pragma unroll
-        for (int i = 0; i < PROJ_CB; ++i) w[i] = W[static_cast<int64_t>(c + i) * d_I + j];
-    }
-}
+template <int ROWS>
+struct ProjLds {
+    float xs[ROWS][PROJ_DMAX];                 // latent rows (reused for the bf16 keys)
+    float wt[PROJ_COLS][PROJ_DMAX + 4];        // W slice, [column][channel]
+};
 
-template <bool BF16, int RPT>
-__device__ __forceinline__ void project_rows(const void* __restrict__ x, int64_t n_rows, int D,
-                                             const int64_t* __restrict__ dst_row, int64_t n_cache_rows,
-                                             const float* __restrict__ W, int d_I, uint4* __restrict__ kcache,
-                                             int64_t row0, float* xs) {
-    constexpr int ROWS = 2 * RPT;
+template <bool BF16, int ROWS>
+__device__ __forceinline__ void project_slice(const void* __restrict__ x, int64_t n_rows, int D,
+                                              const int64_t* __restrict__ dst_row, int64_t n_cache_rows,
+                                              const float* __restrict__ W, int d_I, uint4* __restrict__ kcache,
+                                              int64_t row0, int j0, ProjLds<ROWS>& sh) {
+    constexpr int NT = ROWS * PROJ_COLS;
     const int tid = threadIdx.x;
     const int nr = static_cast<int>(min<int64_t>(ROWS, n_rows - row0));
-    // Stage the rows as float32 (missing rows of a last group read as zero).
-    for (int i = tid; i < ROWS * D; i += PROJ_THREADS) {
-        const int r = i / D, c = i - r * D;
-        float v = 0.0f;
+    // weight slice: thread -> (channel, column quad); quads past d_I are zero
+    for (int i = tid; i < D * (PROJ_COLS / 4); i += NT) {
+        const int c = i >> 3, g = i & 7;
+        const int j = j0 + 4 * g;
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (j < d_I) v = *reinterpret_cast<const float4*>(W + static_cast<int64_t>(c) * d_I + j);
+        sh.wt[4 * g][c] = v.x; sh.wt[4 * g + 1][c] = v.y; sh.wt[4 * g + 2][c] = v.z; sh.wt[4 * g + 3][c] = v.w;
+    }
+    // latent rows, widened to float32 (rows past the end read as zero)
+    for (int i = tid; i < ROWS * (D / 8); i += NT) {
+        const int r = i / (D / 8), c = (i - r * (D / 8)) * 8;
+        float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         if (r < nr) {
             const int64_t g = (row0 + r) * D + c;
-            v = BF16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(x)[g]) << 16)
-                     : static_cast<const float*>(x)[g];
-        }
-        xs[i] = v;
-    }
-    __syncthreads();
-    // Unit u: column j = u % d_I, rows (u / d_I)*RPT .. +RPT-1.  Results go to
-    // the bfloat16 tile ks [ROWS][d_I] behind the staged rows.
-    uint16_t* ks = reinterpret_cast<uint16_t*>(xs + ROWS * D);
-    for (int u = tid; u < d_I * 2; u += PROJ_THREADS) {
-        const int j = u % d_I, g = u / d_I;
-        const float* xr = xs + g * RPT * D;
-        float acc[RPT];
+            if (BF16) {
+                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + g);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) acc[r] = 0.0f;
-        float wr[PROJ_PF][PROJ_CB];
-#pragma unroll
-        for (int b = 0; b < PROJ_PF; ++b) load_wblock(wr[b], W, b * PROJ_CB, D, d_I, j);
-        for (int c0 = 0; c0 < D; c0 += PROJ_PF * PROJ_CB) {
-#pragma unroll
-            for (int b = 0; b < PROJ_PF; ++b) {
-                const int c = c0 + b * PROJ_CB;
-                if (c < D) {
-#pragma unroll
-                    for (int r = 0; r < RPT; ++r) {
-                        float a = acc[r];
-#pragma unroll
-                        for (int q = 0; q < PROJ_CB / 4; ++q) {
-                            const float4 xv = *reinterpret_cast<const float4*>(xr + r * D + c + 4 * q);
-                            a = __builtin_fmaf(xv.x, wr[b][4 * q], a);
-                            a = __builtin_fmaf(xv.y, wr[b][4 * q + 1], a);
-                            a = __builtin_fmaf(xv.z, wr[b][4 * q + 2], a);
-                            a = __builtin_fmaf(xv.w, wr[b][4 * q + 3], a);
-                        }
-                        acc[r] = a;
-                    }
-                    load_wblock(wr[b], W, c + PROJ_PF * PROJ_CB, D, d_I, j);
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = __uint_as_float(ww[e] << 16);
+                    v[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
                 }
+            } else {
+                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + g);
+                const float4 a = p[0], b = p[1];
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
             }
         }
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) ks[(g * RPT + r) * d_I + j] = bf16_nearest_finite(acc[r]);
+        *reinterpret_cast<float4*>(&sh.xs[r][c]) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(&sh.xs[r][c + 4]) = make_float4(v[4], v[5], v[6], v[7]);
     }
     __syncthreads();
+    // one chain per thread: row r, column j0 + jj
+    const int r = tid >> 5, jj = tid & 31;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < D; c += 4) {
+        const float4 xv = *reinterpret_cast<const float4*>(&sh.xs[r][c]);
+        const float4 wv = *reinterpret_cast<const float4*>(&sh.wt[jj][c]);
+        acc = __builtin_fmaf(xv.x, wv.x, acc);
+        acc = __builtin_fmaf(xv.y, wv.y, acc);
+        acc = __builtin_fmaf(xv.z, wv.z, acc);
+        acc = __builtin_fmaf(xv.w, wv.w, acc);
+    }
+    __syncthreads();                    // every chain is done reading xs: reuse it for the keys
+    uint16_t* ks = reinterpret_cast<uint16_t*>(&sh.xs[0][0]);     // [ROWS][PROJ_COLS]
+    ks[r * PROJ_COLS + jj] = bf16_nearest_finite(acc);
+    __syncthreads();
     const int nch = d_I / 8;
-    for (int i = tid; i < nr * nch; i += PROJ_THREADS) {
-        const int r = i / nch, ch = i - r * nch;
-        const int64_t dst = dst_row[row0 + r];
-        if (dst < 0 || dst >= n_cache_rows) continue;
-        kcache[((dst >> 6) * nch + ch) * 64 + (dst & 63)] =
-            *reinterpret_cast<const uint4*>(ks + r * d_I + ch * 8);
+    if (tid < ROWS * (PROJ_COLS / 8)) {
+        const int rr = tid >> 2, q = tid & 3;
+        const int ch = j0 / 8 + q;
+        if (rr < nr && ch < nch) {
+            const int64_t dst = dst_row[row0 + rr];
+            if (dst >= 0 && dst < n_cache_rows)
+                kcache[((dst >> 6) * nch + ch) * 64 + (dst & 63)] =
+                    *reinterpret_cast<const uint4*>(ks + rr * PROJ_COLS + 8 * q);
+        }
     }
 }
 
-// One launch: workgroups [0, nq) quantise 256 (row, block) units each, the
-// rest project 2*RPT rows each.
-template <bool BF16, int RPT>
-__global__ __launch_bounds__(PROJ_THREADS) void kv_write_project_kernel(
+// One launch: workgroups [0, nq) quantise 256 (row, block) units each (with
+// their first 256 threads), the rest project one (ROWS-row, 32-column) tile
+// each: tile pb covers rows ROWS (pb / ncs) and columns 32 (pb % ncs).
+template <bool BF16, int ROWS>
+__global__ __launch_bounds__(ROWS * PROJ_COLS) void kv_write_project_kernel(
     const void* __restrict__ x, int64_t n_rows, int D, const int64_t* __restrict__ dst_row,
     int64_t n_cache_rows, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    const float* __restrict__ W, int d_I, uint4* __restrict__ kcache, int64_t nq) {
-    extern __shared__ float xs[];
+    const float* __restrict__ W, int d_I, uint4* __restrict__ kcache, int64_t nq, int ncs) {
+    __shared__ __attribute__((aligned(16))) ProjLds<ROWS> sh;
     if (blockIdx.x < nq) {
+        if (threadIdx.x >= PROJ_QTHREADS) return;
         const int nblk = D / 16;
-        const int64_t gid = static_cast<int64_t>(blockIdx.x) * PROJ_THREADS + threadIdx.x;
+        const int64_t gid = static_cast<int64_t>(blockIdx.x) * PROJ_QTHREADS + threadIdx.x;
         if (gid >= n_rows * nblk) return;
         const int64_t row = gid / nblk;
         const int blk = static_cast<int>(gid % nblk);
@@ -248,8 +251,10 @@ __global__ __launch_bounds__(PROJ_THREADS) void kv_write_project_kernel(
         quantise_block<BF16>(x, row, blk, D, dst, codes, scales);
         return;
     }
-    const int64_t row0 = (static_cast<int64_t>(blockIdx.x) - nq) * (2 * RPT);
-    project_rows<BF16, RPT>(x, n_rows, D, dst_row, n_cache_rows, W, d_I, kcache, row0, xs);
+    const int64_t pb = static_cast<int64_t>(blockIdx.x) - nq;
+    const int64_t row0 = (pb / ncs) * ROWS;
+    const int j0 = static_cast<int>(pb % ncs) * PROJ_COLS;
+    project_slice<BF16, ROWS>(x, n_rows, D, dst_row, n_cache_rows, W, d_I, kcache, row0, j0, sh);
 }
 
 }  // namespace
@@ -274,43 +279,35 @@ hipError_t launch_kv_write(const void* x, bool x_bf16, int64_t n_rows, int D, co
 
 namespace csa2 {
 
-size_t kv_project_lds_bytes(int D, int d_I, int rpt) {
-    return static_cast<size_t>(2 * rpt) * D * sizeof(float) + static_cast<size_t>(2 * rpt) * d_I * 2;
-}
-
 bool kv_project_shape_supported(int D, int d_I) {
-    return D % 16 == 0 && D > 0 && d_I % 8 == 0 && d_I > 0 && kv_project_lds_bytes(D, d_I, PROJ_MAX_RPT) <= 65536;
+    return D % 16 == 0 && D > 0 && D <= PROJ_DMAX && d_I % 8 == 0 && d_I > 0;
 }
 
-template <int RPT>
+template <int ROWS>
 static hipError_t launch_project(const void* x, bool x_bf16, int64_t n_rows, int D, const int64_t* dst_row,
                                  int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const float* W, int d_I,
                                  void* kcache, hipStream_t st) {
-    const int64_t nq = (n_rows * (D / 16) + PROJ_THREADS - 1) / PROJ_THREADS;
-    const int64_t np = (n_rows + 2 * RPT - 1) / (2 * RPT);
+    const int64_t nq = (n_rows * (D / 16) + PROJ_QTHREADS - 1) / PROJ_QTHREADS;
+    const int ncs = (d_I + PROJ_COLS - 1) / PROJ_COLS;
+    const int64_t np = (n_rows + ROWS - 1) / ROWS * ncs;
     const dim3 grid(static_cast<unsigned>(nq + np));
-    const size_t lds = kv_project_lds_bytes(D, d_I, RPT);
     uint4* kc = static_cast<uint4*>(kcache);
     if (x_bf16)
-        kv_write_project_kernel<true, RPT><<<grid, PROJ_THREADS, lds, st>>>(x, n_rows, D, dst_row, n_cache_rows,
-                                                                            codes, scales, W, d_I, kc, nq);
+        kv_write_project_kernel<true, ROWS><<<grid, ROWS * PROJ_COLS, 0, st>>>(x, n_rows, D, dst_row, n_cache_rows,
+                                                                               codes, scales, W, d_I, kc, nq, ncs);
     else
-        kv_write_project_kernel<false, RPT><<<grid, PROJ_THREADS, lds, st>>>(x, n_rows, D, dst_row, n_cache_rows,
-                                                                             codes, scales, W, d_I, kc, nq);
+        kv_write_project_kernel<false, ROWS><<<grid, ROWS * PROJ_COLS, 0, st>>>(x, n_rows, D, dst_row, n_cache_rows,
+                                                                                codes, scales, W, d_I, kc, nq, ncs);
     return hipGetLastError();
 }
 
-// A few rows (a decode token's batch): one row per thread, many workgroups.
-// Thousands (a prefill chunk's entries): eight rows per thread, so each
-// weight read serves eight fmas.
 hipError_t launch_kv_write_project(const void* x, bool x_bf16, int64_t n_rows, int D, const int64_t* dst_row,
                                    int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const float* W,
                                    int d_I, void* kcache, hipStream_t st) {
     if (n_rows == 0) return hipSuccess;
-    if (n_rows <= 1024)
-        return launch_project<1>(x, x_bf16, n_rows, D, dst_row, n_cache_rows, codes, scales, W, d_I, kcache, st);
-    return launch_project<PROJ_MAX_RPT>(x, x_bf16, n_rows, D, dst_row, n_cache_rows, codes, scales, W, d_I,
-                                        kcache, st);
+    if (n_rows <= 512)
+        return launch_project<8>(x, x_bf16, n_rows, D, dst_row, n_cache_rows, codes, scales, W, d_I, kcache, st);
+    return launch_project<32>(x, x_bf16, n_rows, D, dst_row, n_cache_rows, codes, scales, W, d_I, kcache, st);
 }
 
 }  // namespace csa2

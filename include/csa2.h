@@ -100,12 +100,13 @@ int mxfp4_kv_write(const void *x, int x_dtype, int64_t n_rows, int32_t D,
  * dst_row     [n_rows] int64 flat destination rows; rows outside
  *             [0, n_cache_rows) are skipped (codes, scales and key alike)
  * codes, scales  as mxfp4_kv_write
- * w_ik        [D][d_I] float32 projection weights, row-major (device)
+ * w_ik        [D][d_I] float32 projection weights, row-major (device), 16-byte aligned
  * idx_k_cache bfloat16, TILED layout (see csa2_index_score), n_cache_rows
  *             rows of d_I; 16-byte aligned
- * Requires D % 16 == 0, d_I % 8 == 0, n_cache_rows % 64 == 0, and
- * 64*D + 32*d_I <= 65536 (LDS for a 16-row group; D = 512 allows d_I <= 1024),
- * else CSA2_E_UNSUPPORTED.  Caller owns every buffer; nothing is allocated.
+ * Requires D % 16 == 0, d_I % 8 == 0, n_cache_rows % 64 == 0 (else
+ * CSA2_E_INVALID), D <= 512 (else CSA2_E_UNSUPPORTED: a workgroup keeps 32
+ * latent rows and a 32-column weight slice in LDS), and x, w_ik and
+ * idx_k_cache 16-byte aligned.  Caller owns every buffer; nothing is allocated.
  * ------------------------------------------------------------------------ */
 int csa2_kv_write_project(const void *x, int x_dtype, int64_t n_rows, int32_t D,
                           const int64_t *dst_row, int64_t n_cache_rows, uint8_t *codes,

@@ -164,7 +164,7 @@ def test_kv_write_project_rejects_bad_arguments_on_host():
     rc = L.csa2_kv_write_project(p, 0, 4, 512, p, 100, p, p, p, 128, p, None)
     assert rc == 1 and "% 64" in _err()
     rc = L.csa2_kv_write_project(p, 0, 4, 1024, p, 64, p, p, p, 128, p, None)
-    assert rc == 2 and "LDS" in _err()
+    assert rc == 2 and "D <= 512" in _err()
     rc = L.csa2_kv_write_project(p, 0, 4, 512, p, 64, p, p, None, 128, p, None)
     assert rc == 1 and "null" in _err()
     assert L.csa2_kv_write_project(None, 0, 0, 512, None, 64, None, None, None, 128, None, None) == 0

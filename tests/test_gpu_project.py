@@ -61,13 +61,15 @@ def test_project_decode_batch_bf16(K):
 
 
 def test_project_fp32_rows_and_ragged_group(K):
-    # 37 rows: two full 16-row groups and a ragged tail of 5
+    # 37 rows (8-row tiles below 513 rows): four full tiles and a ragged one of 5
     _case(K, 32, 37, 512, 128, 256, torch.float32)
 
 
 def test_project_tiny_shape_and_single_row(K):
     _case(K, 33, 1, 64, 32, 64, torch.float32)
     _case(K, 34, 19, 64, 32, 64, torch.float32)
+    # a column count that is not a multiple of the 32-column slice
+    _case(K, 39, 21, 128, 40, 64, torch.bfloat16)
 
 
 def test_project_skips_rows_outside_the_cache(K):
@@ -83,7 +85,7 @@ def test_project_prefill_chunk_entries(K):
 
 
 def test_project_many_rows_ragged_group(K):
-    # more than 1,024 rows take eight rows per thread; 1,100 leaves a group of 12
+    # 1,100 rows (32-row tiles above 512 rows): 34 full tiles and a ragged one of 12
     n, cap = 1100, 2048
     dst = torch.randperm(cap, generator=torch.Generator().manual_seed(38))[:n].to(torch.int64)
     dst[17] = -1
