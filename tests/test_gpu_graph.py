@@ -67,3 +67,69 @@ def test_decode_step_graph_replays_match_eager(K):
         got = _snapshot(step)
         for a, b in zip(got, want):
             assert torch.equal(a, b), rep
+
+
+def _replay_check(make_call, outs, clobber, reps=3):
+    """Capture make_call() into a graph; each replay (after eager work that
+    clobbers what the call writes) must reproduce the eager outputs bit for
+    bit.  outs() returns the written values."""
+    make_call()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        make_call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        make_call()
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        clobber()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for w, o in zip(want, outs()):
+            assert torch.equal(w, o), rep
+
+
+def test_kv_write_project_graph_replays_match_eager(K):
+    dev = torch.device("cuda:0")
+    n, D, d_I, cap = 64, 512, 128, 1024
+    x = ci.gaussian(601, ci.TID_KV, (n, D), dtype=torch.bfloat16, clip=ci.NORM_BOUND).to(dev)
+    w_ik = (ci.gaussian(601, ci.TID_W_IK, (D, d_I)) / 22.627).to(dev)
+    dst = (torch.arange(n, dtype=torch.int64) * 16 + 3).to(dev)
+    codes = torch.zeros((cap, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((cap, D // 16), dtype=torch.uint8, device=dev)
+    kc = torch.zeros((1, cap, d_I), dtype=torch.bfloat16, device=dev)
+
+    def clobber():                      # every byte the call writes, and more
+        codes.fill_(0x5A)
+        scales.fill_(0xA5)
+        kc.fill_(3.0)
+
+    def written():
+        return [codes[dst], scales[dst], K.untile_indexer_cache(kc)[0][dst]]
+
+    _replay_check(lambda: K.csa2_kv_write_project(x, dst, codes, scales, w_ik, kc), written, clobber)
+
+
+def test_mhc_step_graph_replays_match_eager(K):
+    import math
+    dev = torch.device("cuda:0")
+    T, n, d = 200, 4, 1024
+    X = ci.gaussian(602, ci.TID_MHC_X, (T, n, d), dtype=torch.bfloat16).to(dev)
+    f = ci.gaussian(602, ci.TID_MHC_F, (T, d), dtype=torch.bfloat16).to(dev)
+    coef = ci.uniform(602, ci.TID_MHC_COEF, (T, 24)).to(dev)
+    A, B, C = coef[:, :4].contiguous(), (0.5 * coef[:, 4:20]).reshape(T, 4, 4).contiguous(), (2 * coef[:, 20:]).contiguous()
+    phiT = (ci.gaussian(602, ci.TID_MHC_PHI, (24, n * d)) / math.sqrt(n * d)).to(torch.bfloat16).to(dev)
+    bias = (0.5 * ci.gaussian(603, ci.TID_MHC_PHI, (24,))).to(dev)
+    out = (torch.empty_like(X), torch.empty_like(f), torch.empty_like(A), torch.empty_like(B), torch.empty_like(C))
+
+    def clobber():
+        for o in out:
+            o.fill_(-1.0)
+
+    _replay_check(lambda: K.csa2_mhc_step(X, f, A, B, C, phiT, bias, (1.0, 1.0, 1.0), iters=20, out=out),
+                  lambda: list(out), clobber)
