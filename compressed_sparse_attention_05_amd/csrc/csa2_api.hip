@@ -422,6 +422,8 @@ int csa2_mhc_step(const csa2_mhc_args* m, void* stream) {
     if (!aligned(m->X, 16) || !aligned(m->f, 16) || !aligned(m->phiT, 16) || !aligned(m->X_next, 16) ||
         !aligned(m->u_next, 16))
         return fail(CSA2_E_INVALID, "csa2_mhc_step: X, f, phiT, X_next and u_next must be 16-byte aligned");
+    if (m->X_next == m->X || m->u_next == m->f)
+        return fail(CSA2_E_INVALID, "csa2_mhc_step: X_next and u_next must not alias X and f");
     csa2::MhcLaunch p;
     p.X = static_cast<const uint16_t*>(m->X); p.f = static_cast<const uint16_t*>(m->f);
     p.A = m->A; p.B = m->B; p.C = m->C;

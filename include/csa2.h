@@ -399,7 +399,8 @@ int csa2_decode_select(const csa2_decode_select_args *a, void *ws, size_t ws_byt
  *   X, X_next [T][n][d] bf16;  f, u_next [T][d] bf16;  phiT [2n+n^2][n*d] bf16;
  *   A, A_next, C, C_next [T][n] f32;  B, B_next [T][n][n] f32;  bias [2n+n^2] f32.
  * Supported: n = 4, d a multiple of 128 (else CSA2_E_UNSUPPORTED).  X, f, phiT,
- * X_next and u_next must be 16-byte aligned.  X_next must not alias X.
+ * X_next and u_next must be 16-byte aligned.  X_next must not alias X, nor u_next
+ * f (CSA2_E_INVALID).
  * ------------------------------------------------------------------------ */
 typedef struct csa2_mhc_args {
     const void *X;       /* [T][n][d] bf16 */

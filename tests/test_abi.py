@@ -168,3 +168,20 @@ def test_kv_write_project_rejects_bad_arguments_on_host():
     rc = L.csa2_kv_write_project(p, 0, 4, 512, p, 64, p, p, None, 128, p, None)
     assert rc == 1 and "null" in _err()
     assert L.csa2_kv_write_project(None, 0, 0, 512, None, 64, None, None, None, 128, None, None) == 0
+
+
+def test_mhc_step_rejects_bad_arguments_on_host():
+    L = binding.lib()
+    p = ctypes.c_void_p(256).value
+    a = binding.MhcArgs(X=p, f=p, A=p, B=p, C=p, phiT=p, bias=p, alpha_pre=1.0, alpha_post=1.0, alpha_res=1.0,
+                        T=4, n=3, d=256, iters=20, X_next=p + 4096, u_next=p + 8192, A_next=p, B_next=p, C_next=p)
+    assert L.csa2_mhc_step(ctypes.byref(a), None) == 2 and "n = 4" in _err()
+    a.n, a.d = 4, 200
+    assert L.csa2_mhc_step(ctypes.byref(a), None) == 2
+    a.d = 256
+    a.X_next = p
+    assert L.csa2_mhc_step(ctypes.byref(a), None) == 1 and "alias" in _err()
+    a.X_next, a.phiT = p + 4096, None
+    assert L.csa2_mhc_step(ctypes.byref(a), None) == 1 and "null" in _err()
+    a.T = 0
+    assert L.csa2_mhc_step(ctypes.byref(a), None) == 0
