@@ -9,6 +9,62 @@
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
+// ---- wave64 scans and reductions on the VALU.  Each step of __shfl_up /
+// __shfl_xor is a ds_bpermute round trip through the LDS crossbar; here DPP
+// row shifts scan each 16-lane row in four dependent VALU ops, and the four
+// row totals come back through readlane.  Every caller runs them with the
+// whole wave active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_shift(uint32_t fill, uint32_t x) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+// inclusive prefix sums within each 16-lane row
+__device__ __forceinline__ uint32_t row_incl_sum(uint32_t x) {
+    x += dpp_shift<kRowShr1>(0u, x);
+    x += dpp_shift<kRowShr2>(0u, x);
+    x += dpp_shift<kRowShr4>(0u, x);
+    x += dpp_shift<kRowShr8>(0u, x);
+    return x;
+}
+__device__ __forceinline__ uint32_t rl(uint32_t x, int lane) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
+}
+// inclusive prefix sum over the wave in lane order
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x = row_incl_sum(x);
+    const uint32_t r0 = rl(x, 15), r1 = rl(x, 31), r2 = rl(x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+// wave-uniform sum, minimum and maximum
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+    x = row_incl_sum(x);
+    return rl(x, 15) + rl(x, 31) + rl(x, 47) + rl(x, 63);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+    uint32_t y;
+    y = dpp_shift<kRowShr1>(0xffffffffu, x); x = y < x ? y : x;
+    y = dpp_shift<kRowShr2>(0xffffffffu, x); x = y < x ? y : x;
+    y = dpp_shift<kRowShr4>(0xffffffffu, x); x = y < x ? y : x;
+    y = dpp_shift<kRowShr8>(0xffffffffu, x); x = y < x ? y : x;
+    const uint32_t a = rl(x, 15), b = rl(x, 31), c = rl(x, 47), d = rl(x, 63);
+    const uint32_t ab = a < b ? a : b, cd = c < d ? c : d;
+    return ab < cd ? ab : cd;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    uint32_t y;
+    y = dpp_shift<kRowShr1>(0u, x); x = y > x ? y : x;
+    y = dpp_shift<kRowShr2>(0u, x); x = y > x ? y : x;
+    y = dpp_shift<kRowShr4>(0u, x); x = y > x ? y : x;
+    y = dpp_shift<kRowShr8>(0u, x); x = y > x ? y : x;
+    const uint32_t a = rl(x, 15), b = rl(x, 31), c = rl(x, 47), d = rl(x, 63);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
 
 __device__ __forceinline__ uint32_t key_of(float v) {
     uint32_t u = __float_as_uint(v);
@@ -48,7 +104,7 @@ __device__ __forceinline__ void hist_inc(uint32_t* hist, uint32_t bin, bool vali
     for (int round = 0; round < 4; ++round) {
         if (active == 0) return;
         const int leader = __builtin_ctzll(active);
-        const uint32_t lb = __shfl(bin, leader);
+        const uint32_t lb = rl(bin, leader);
         const uint64_t same = __ballot(valid && bin == lb) & active;
         if (lane == leader) atomicAdd(&hist[lb], static_cast<uint32_t>(__popcll(same)));
         active &= ~same;
@@ -66,12 +122,7 @@ __device__ void find_digit(const uint32_t* hist, int nbins, uint32_t need, uint3
         const int hi_bin = nbins - 1 - lane * per;
         uint32_t sum = 0;
         for (int i = 0; i < per; ++i) sum += hist[hi_bin - i];
-        uint32_t incl = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
+        const uint32_t incl = wave_incl_sum(sum);
         const uint32_t excl = incl - sum;
         if (excl < need && incl >= need) {
             uint32_t acc = excl;
@@ -181,7 +232,7 @@ __device__ uint32_t count_valid(Get get, int64_t n, uint32_t* wave_tot) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) c += kk[j] != 0u;
     }
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    c = wave_sum(c);
     if ((threadIdx.x & 63) == 0) wave_tot[threadIdx.x >> 6] = c;
     __syncthreads();
     uint32_t tot = 0;
@@ -231,12 +282,7 @@ struct alignas(16) SelLds {
 // the total.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wave_tot, uint32_t& total) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    uint32_t incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
+    const uint32_t incl = wave_incl_sum(v);
     if (lane == 63) wave_tot[wv] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -264,13 +310,9 @@ __device__ __forceinline__ uint32_t sel_stats(const uint32_t (&kk)[R], SelLds& s
         mn = (kk[j] != 0u && kk[j] < mn) ? kk[j] : mn;
         mx = kk[j] > mx ? kk[j] : mx;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        cnt += __shfl_xor(cnt, off);
-        const uint32_t omn = __shfl_xor(mn, off), omx = __shfl_xor(mx, off);
-        mn = omn < mn ? omn : mn;
-        mx = omx > mx ? omx : mx;
-    }
+    cnt = wave_sum(cnt);
+    mn = wave_min(mn);
+    mx = wave_max(mx);
     if (lane == 0) { sh.wave_tot[wv] = cnt; sh.wave_min[wv] = mn; sh.wave_max[wv] = mx; }
     {
         const int hb = kSelBins - 8 - 8 * tid;
@@ -333,8 +375,7 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
             const uint4 lo = *reinterpret_cast<const uint4*>(&hist[hb]);
             const uint4 hi = *reinterpret_cast<const uint4*>(&hist[hb + 4]);
             uint32_t sum = lo.x + lo.y + lo.z + lo.w + hi.x + hi.y + hi.z + hi.w;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            sum = wave_sum(sum);
             if (lane == 0) sh.pass_tot[buf][wv] = sum;
         }
         __syncthreads();
@@ -358,12 +399,7 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
         uint32_t s8 = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) s8 += c[i];
-        uint32_t incl = s8;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
+        const uint32_t incl = wave_incl_sum(s8);
         const uint32_t excl = acc + incl - s8;
         const bool mine = excl < need && excl + s8 >= need;
         uint32_t digit = 0, above = 0, in_bin = 0;
@@ -380,12 +416,12 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
         }
         const uint64_t bal = __ballot(mine);
         const int src = bal ? static_cast<int>(__builtin_ctzll(bal)) : 0;
-        digit = __shfl(digit, src);
-        above = __shfl(above, src);
+        digit = rl(digit, src);
+        above = rl(above, src);
         known = (known << nb) | digit;
         need -= above;
         if (EARLY && shift > 0) {
-            in_bin = __shfl(in_bin, src);
+            in_bin = rl(in_bin, src);
             const uint32_t lowest = static_cast<uint32_t>(known) << shift;
             if (in_bin == need && lowest != 0u) {
                 need = 0;
@@ -420,12 +456,7 @@ __device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, 
 #pragma unroll
     for (int j = 0; j < R; ++j) { above += kk[j] > T; ties += kk[j] == T; }
     const uint32_t packed = (above << 16) | ties;
-    uint32_t incl = packed;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
+    const uint32_t incl = wave_incl_sum(packed);
     if (lane == 63) sh.emit_tot[wv] = incl;
     __syncthreads();
     uint32_t before = 0;
