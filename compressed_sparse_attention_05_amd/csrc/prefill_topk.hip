@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
     // total candidates
     uint32_t part = 0;
     for (int64_t sgi = tid; sgi < n_seg; sgi += kThreads) part += crow[sgi];
-    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    part = wave_sum(part);
     if (lane == 0) wave_tot[wv] = part;
     __syncthreads();
     uint32_t C = 0;
@@ -537,12 +537,7 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
         for (int64_t sb = 0; sb < n_seg; sb += kThreads) {
             const int64_t sgi = sb + tid;
             const uint32_t c = sgi < n_seg ? crow[sgi] : 0u;
-            uint32_t incl = c;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t x = __shfl_up(incl, off);
-                if (lane >= off) incl += x;
-            }
+            const uint32_t incl = wave_incl_sum(c);
             if (lane == 63) wave_tot[wv] = incl;
             __syncthreads();
             uint32_t before = 0, tot = 0;

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
         v += kk[j] != 0u;
         hist_inc(hist, kk[j] >> 20, kk[j] != 0u);
     }
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    v = wave_sum(v);
     if ((threadIdx.x & 63) == 0 && v) atomicAdd(&ws.nvalid[row], v);
     __syncthreads();
     for (int i = threadIdx.x; i < kHistBins; i += kThreads)
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void topk_collect_kernel(const float* __r
     if (tot == 0) return;
     uint32_t wb = 0;
     if (lane == 0) wb = atomicAdd(&ws.cnt[row], tot);
-    wb = __shfl(wb, 0);
+    wb = rl(wb, 0);
 #pragma unroll
     for (int j = 0; j < kChunk / kThreads; ++j) {
         const uint32_t off = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal[j] >> 32),
