@@ -1062,7 +1062,7 @@ SplitPlan plan(int64_t units, int H, int k, int W, int KT) {
 // write-out) plus the combine's reading of the partials.  Fixed at the
 // MI355X CU count, so the workspace size never depends on the device.
 constexpr int kCUs = 256;
-bool use_ws(int64_t units, int D) { return D == 512 && units >= 64; }
+bool use_ws(int64_t units, int D) { return D == 512 && units >= 16; }
 
 SplitPlan plan_ws(int64_t units, int H, int k, int W, int KT) {
     SplitPlan best;
@@ -1110,9 +1110,11 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     a.ws_m = L.ws ? L.ws + nparts * 64 * D : nullptr;
     a.ws_l = L.ws ? a.ws_m + nparts * 64 : nullptr;
     if (L.units == 0) return hipSuccess;
-    // many query units (prefill chunks, large batches): the warp-specialised
-    // kernel keeps the matrix cores busier; few units: the split kernel has
-    // the shorter start-up
+    // 16 or more query units (prefill chunks, decode batches of 16+): the
+    // warp-specialised kernel keeps the matrix cores busier (MI355X, 64
+    // heads, k = 2048: 28.8 against 42.0 us at 16 units, 39.4 against 56.4 us
+    // at 32); at 8 units the split kernel's shorter start-up wins (23.4
+    // against 24.7 us)
     if (use_ws(L.units, D))
         attn_ws_kernel<BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 512, 0, st>>>(a);
     else

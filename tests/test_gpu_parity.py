@@ -352,12 +352,14 @@ def test_attention_d512_k2048_split(K):
 
 
 def test_attention_many_units_warp_specialised(K):
-    # 64 or more query units take the warp-specialised kernel: a tile that
+    # 16 or more query units take the warp-specialised kernel: a tile that
     # straddles the main/window boundary (k = 333), ragged windows, -1
     # entries and duplicates, in bf16 and float32, one and two head blocks
     lens = [(7 * b) % 129 for b in range(64)]
     _attn_case(K, 203, B=64, N=3000, D=512, H=64, k=333, W=128, swa_lens=lens, dup=True)
     _attn_case(K, 204, B=64, N=2000, D=512, H=128, k=256, W=128, swa_lens=[128] * 64, dtype=torch.float32)
+    # the smallest batch on this kernel, with several key splits per unit
+    _attn_case(K, 205, B=16, N=4000, D=512, H=64, k=1500, W=128, swa_lens=[(11 * b) % 129 for b in range(16)])
 
 
 def test_attention_empty_set_is_zero(K):
