@@ -49,14 +49,9 @@ __device__ __forceinline__ uint32_t mag_code(float a, float s) {
     return c;
 }
 
-// Quantise block `blk` (16 channels) of input row `row` into flat cache row
-// `dst`: scale byte, then eight code bytes (channel 2j in the low nibble).
+// The 16 channels of block `blk` of input row `row`, widened to float32.
 template <bool BF16>
-__device__ __forceinline__ void quantise_block(const void* __restrict__ x, int64_t row, int blk, int D,
-                                               int64_t dst, uint8_t* __restrict__ codes,
-                                               uint8_t* __restrict__ scales) {
-    const int nblk = D / 16;
-    float v[16];
+__device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t row, int blk, int D, float (&v)[16]) {
     if (BF16) {
         const uint4* p = reinterpret_cast<const uint4*>(
             static_cast<const uint16_t*>(x) + row * D + blk * 16);
@@ -76,6 +71,13 @@ __device__ __forceinline__ void quantise_block(const void* __restrict__ x, int64
             v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
         }
     }
+}
+
+// Quantise one 16-channel block v into flat cache row `dst`: scale byte,
+// then eight code bytes (channel 2j in the low nibble).
+__device__ __forceinline__ void quantise_block(const float (&v)[16], int blk, int D, int64_t dst,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int nblk = D / 16;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -111,16 +113,19 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
         if (gid >= n_rows * nch) return;
         const int64_t row = gid / nch;
         const int c = static_cast<int>(gid % nch);
+        const uint4 val = krows[row * nch + c];
         const int64_t r = dst_row[row];
         if (r < 0 || r >= n_cache_rows) return;
-        kcache[((r >> 6) * nch + c) * 64 + (r & 63)] = krows[row * nch + c];
+        kcache[((r >> 6) * nch + c) * 64 + (r & 63)] = val;
         return;
     }
     const int64_t row = gid / nblk;
     const int blk = static_cast<int>(gid % nblk);
+    float v[16];
+    load_block<BF16>(x, row, blk, D, v);           // issued together with the dst_row load
     const int64_t dst = dst_row[row];
     if (dst < 0 || dst >= n_cache_rows) return;
-    quantise_block<BF16>(x, row, blk, D, dst, codes, scales);
+    quantise_block(v, blk, D, dst, codes, scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,9 +251,11 @@ __global__ __launch_bounds__(ROWS * PROJ_COLS) void kv_write_project_kernel(
         if (gid >= n_rows * nblk) return;
         const int64_t row = gid / nblk;
         const int blk = static_cast<int>(gid % nblk);
+        float v[16];
+        load_block<BF16>(x, row, blk, D, v);
         const int64_t dst = dst_row[row];
         if (dst < 0 || dst >= n_cache_rows) return;
-        quantise_block<BF16>(x, row, blk, D, dst, codes, scales);
+        quantise_block(v, blk, D, dst, codes, scales);
         return;
     }
     const int64_t pb = static_cast<int64_t>(blockIdx.x) - nq;
