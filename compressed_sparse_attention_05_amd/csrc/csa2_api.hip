@@ -329,6 +329,9 @@ int check_prefill_topk(const csa2_prefill_topk_args* a) {
         return fail(CSA2_E_INVALID, "%s: null tensor", fn);
     if (!aligned(a->q_idx, 16) || !aligned(a->k_idx, 16))
         return fail(CSA2_E_INVALID, "%s: q_idx and k_idx must be 16-byte aligned", fn);
+    if (csa2::prefill_cols(a->T, a->ctx_len, a->q_pos0, a->m) > csa2::prefill_topk_max_cols())
+        return fail(CSA2_E_UNSUPPORTED, "%s: more than %lld visible entries", fn,
+                    static_cast<long long>(csa2::prefill_topk_max_cols()));
     return CSA2_OK;
 }
 

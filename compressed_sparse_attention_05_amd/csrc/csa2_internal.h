@@ -84,6 +84,10 @@ struct PrefillLaunch {
 };
 size_t prefill_topk_workspace_bytes(int64_t T, int32_t ctx_len, int64_t q_pos0, int32_t m);
 int prefill_topk_max_k();
+// most visible entries a prefill chunk may have (a wave's 8 candidate rows
+// stay one buffer range below 2^31 bytes)
+int64_t prefill_topk_max_cols();
+int64_t prefill_cols(int64_t T, int32_t ctx_len, int64_t q_pos0, int32_t m);
 hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st);
 
 struct DecodeSelectLaunch {

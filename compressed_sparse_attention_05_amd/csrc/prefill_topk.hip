@@ -56,6 +56,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeads = 8, kDim = 128;          // indexer shape of the matrix-core path
 constexpr int kNch = kDim * 2 / 16;            // 16-byte chunks per indexer row
@@ -211,17 +212,13 @@ __device__ __forceinline__ float relu(float x) {
     return __int_as_float(i > 0 ? i : 0);
 }
 
-constexpr int kStage = kTileKeys;              // staged candidates per query row per tile (<= its keys)
-
 template <bool SAMPLE>
 __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, int64_t t1, int64_t n_cols, Geo g,
                                                          float* __restrict__ samp, int64_t ld_s,
                                                          const uint32_t* __restrict__ thr,
                                                          uint32_t* __restrict__ counts, uint2* __restrict__ cand) {
     constexpr int KROW = kDim + 8;               // padded LDS row (bf16 elements)
-    constexpr int kStageWords = SAMPLE ? 1 : 8 * (8 * kStage + 64);   // per wave: 8 rows + one dummy slot per lane
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTileKeys * KROW];
-    __shared__ __attribute__((aligned(16))) uint2 stage_all[SAMPLE ? 1 : kStageWords];
     int64_t bx;
     int by;
     {
@@ -273,11 +270,13 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
             for (int i = 0; i < 4; ++i) wr[mt][4 * qq + i] = a.w[t * kHeads + 4 * (lane >> 5) + i];
         }
     // per lane and (mt, e): its query's visible limit minus lane%32 (key
-    // block jb is visible for this lane while jb < lim), threshold, and the
-    // staging slots of its row (row index 4mt + query within the M-tile)
+    // block jb is visible for this lane while jb < lim), threshold, and
+    // where its row's values go (the sample row, or the workgroup's first
+    // candidate slot of the row)
     int32_t lim[2][2];
     float thf[2][2];
     float* sbase[2][2];
+    uint32_t coff[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -290,12 +289,19 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
             lim[mt][e] = static_cast<int32_t>(v - (lane & 31));
             thf[mt][e] = SAMPLE ? 0.0f : thr_float(thr[tc - t0]);
             sbase[mt][e] = SAMPLE ? samp + (tc - t0) * ld_s + (lane & 31) : nullptr;
+            coff[mt][e] = static_cast<uint32_t>(((4 * mt + (hi ? 2 + e : e)) * g.cand_ld + bx * (kSub * g.blocks)) * 8);
         }
-    uint2* stage = stage_all + (SAMPLE ? 0 : wv * (8 * kStage + 64));
-    // uniform counters per wave row (4mt + query): staged this tile, emitted so far
-    uint32_t c_tile[8], c_glob[8];
+    // the wave's 8 candidate rows as one buffer (byte range below 2^31,
+    // which the launch checks; rows past the chunk are outside the range)
+    int64_t rows_here = t1 - qb;
+    rows_here = rows_here < 0 ? 0 : (rows_here > 8 ? 8 : rows_here);
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+        SAMPLE ? static_cast<void*>(samp) : static_cast<void*>(cand + (qb < t1 ? qb - t0 : 0) * g.cand_ld),
+        static_cast<short>(0), SAMPLE ? 0 : static_cast<int>(rows_here * g.cand_ld * 8), 0x00020000);
+    // uniform count of candidates emitted so far per wave row (4mt + query)
+    uint32_t c_glob[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) { c_tile[q] = 0; c_glob[q] = 0; }
+    for (int q = 0; q < 8; ++q) c_glob[q] = 0;
 
     // tile loader: thread -> chunk c = tid / 32 of key (tid % 32) in each of
     // the tile's 4 column blocks.  Consecutive candidate tiles are 128 keys
@@ -324,84 +330,106 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
         *reinterpret_cast<uint4*>(d + 2 * kSub * KROW) = n2;
         *reinterpret_cast<uint4*>(d + 3 * kSub * KROW) = n3;
     };
+    // column block i of the tile in LDS buffer buf -> two 32 x 32 s tiles
+    auto mfma_block = [&](int buf, int i, floatx16* acc) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const bf16x8 kb = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(kSub * i + (lane & 31)) * KROW + 16 * s +
+                                                                 8 * (lane >> 5)]));
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb, acc[1], 0, 0, 0);
+        }
+    };
+    // s~ of column block b (keys from jb) and what becomes of it; every block
+    // is computed (loads of keys past the end read row 0) and invisible keys
+    // are masked here
+    auto epilogue = [&](const floatx16* acc, int b) {
+        const int64_t jb = block_key(b);
+        const int32_t jb32 = static_cast<int32_t>(jb < 0x7fffffff ? jb : 0x7fffffff);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            float part[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                float p = wr[mt][4 * qq] * relu(acc[mt][4 * qq]);
+#pragma unroll
+                for (int h = 1; h < 4; ++h) p = fmaf(wr[mt][4 * qq + h], relu(acc[mt][4 * qq + h]), p);
+                part[qq] = p;
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[e]),
+                                                                 __float_as_uint(part[2 + e]), false, false);
+                const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const bool vis_ok = jb32 < lim[mt][e];
+                if (SAMPLE) {
+                    const int64_t gi = jb / kGroup;
+                    if (gi * kSub < ld_s) sbase[mt][e][gi * kSub] = vis_ok ? v : -__builtin_inff();
+                } else {
+                    // (s~ bits, position) of taken keys go straight to the
+                    // row's next slots, in position order: the lower half of
+                    // the wave holds row qlo, the upper half row qhi.  Lanes
+                    // that take nothing store past the buffer's range, which
+                    // the hardware drops, so the store needs no branch.
+                    const bool take = vis_ok && v >= thf[mt][e];
+                    const uint64_t bal = __ballot(take);
+                    const uint32_t blo = static_cast<uint32_t>(bal), bhi = static_cast<uint32_t>(bal >> 32);
+                    const uint32_t n_lo = static_cast<uint32_t>(__builtin_popcount(blo));
+                    const uint32_t n_hi = static_cast<uint32_t>(__builtin_popcount(bhi));
+                    const int qlo = 4 * mt + e, qhi = 4 * mt + 2 + e;
+                    const uint32_t base = hi ? c_glob[qhi] - n_lo : c_glob[qlo];
+                    const uint32_t at = __builtin_amdgcn_mbcnt_hi(bhi, __builtin_amdgcn_mbcnt_lo(blo, base));
+                    // (every real offset is below 2^31; bit 31 marks the rest)
+                    const uint32_t off = (coff[mt][e] + 8u * at) | (static_cast<uint32_t>(!take) << 31);
+                    u32x2 val;
+                    val[0] = __float_as_uint(v);
+                    val[1] = static_cast<uint32_t>(jb32) + (lane & 31);
+                    __builtin_amdgcn_raw_buffer_store_b64(val, crsrc, static_cast<int>(off), 0, 0);
+                    c_glob[qlo] += n_lo;
+                    c_glob[qhi] += n_hi;
+                }
+            }
+        }
+    };
+
+    // software pipeline: the matrix products of column block b + 1 are
+    // issued beside the epilogue of block b (two accumulator sets, blocks
+    // alternate between them; 4 blocks per tile keep the parity per tile)
+    floatx16 acc0[2], acc1[2];
+    // one matrix product, then a share of the other block's epilogue: in-order
+    // issue would otherwise run the 16 products first and the epilogue after
+    auto interleave = [&]() {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);    // VALU
+        }
+    };
     load_tile(0);
     store_tile(0);
     __syncthreads();
+    mfma_block(0, 0, acc0);
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int buf = tile & 1;
         if (tile + 1 < n_tiles) load_tile(tile + 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // every block is computed (loads of keys past the end read row 0);
-            // invisible keys are masked below
-            const int64_t jb = block_key(4 * tile + i);
-            floatx16 acc[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const bf16x8 kb = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(kSub * i + (lane & 31)) * KROW + 16 * s +
-                                                                     8 * (lane >> 5)]));
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kb, acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kb, acc[1], 0, 0, 0);
-            }
-            const int32_t jb32 = static_cast<int32_t>(jb < 0x7fffffff ? jb : 0x7fffffff);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                float part[4];
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    float p = wr[mt][4 * qq] * relu(acc[mt][4 * qq]);
-#pragma unroll
-                    for (int h = 1; h < 4; ++h) p = fmaf(wr[mt][4 * qq + h], relu(acc[mt][4 * qq + h]), p);
-                    part[qq] = p;
-                }
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[e]),
-                                                                     __float_as_uint(part[2 + e]), false, false);
-                    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                    const bool vis_ok = jb32 < lim[mt][e];
-                    if (SAMPLE) {
-                        const int64_t gi = jb / kGroup;
-                        if (gi * kSub < ld_s) sbase[mt][e][gi * kSub] = vis_ok ? v : -__builtin_inff();
-                    } else {
-                        // stage (s~ bits, position) of taken keys in row order;
-                        // lanes that take nothing write their dummy slot
-                        const bool take = vis_ok && v >= thf[mt][e];
-                        const uint64_t bal = __ballot(take);
-                        const uint32_t blo = static_cast<uint32_t>(bal), bhi = static_cast<uint32_t>(bal >> 32);
-                        const uint32_t n_lo = static_cast<uint32_t>(__builtin_popcount(blo));
-                        const uint32_t n_hi = static_cast<uint32_t>(__builtin_popcount(bhi));
-                        const int qlo = 4 * mt + e, qhi = 4 * mt + 2 + e;
-                        const uint32_t base = hi ? qhi * kStage + c_tile[qhi] - n_lo : qlo * kStage + c_tile[qlo];
-                        const uint32_t at = __builtin_amdgcn_mbcnt_hi(bhi, __builtin_amdgcn_mbcnt_lo(blo, base));
-                        const uint32_t slot = take ? at : 8 * kStage + lane;
-                        stage[slot] = make_uint2(__float_as_uint(v), static_cast<uint32_t>(jb32) + (lane & 31));
-                        c_tile[qlo] += n_lo;
-                        c_tile[qhi] += n_hi;
-                    }
-                }
-            }
-        }
-        if (!SAMPLE) {
-            // flush the staged candidates of the wave's 8 rows to their slot ranges
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int64_t t = qb + q;
-                if (c_tile[q] > 0u && t < t1) {
-                    uint2* dst = cand + (t - t0) * g.cand_ld + bx * (kSub * g.blocks) + c_glob[q];
-                    for (uint32_t x = lane; x < c_tile[q]; x += 64) dst[x] = stage[q * kStage + x];
-                }
-                c_glob[q] += c_tile[q];
-                c_tile[q] = 0;
-            }
-        }
+        mfma_block(buf, 1, acc1);
+        epilogue(acc0, 4 * tile + 0);
+        interleave();
+        mfma_block(buf, 2, acc0);
+        epilogue(acc1, 4 * tile + 1);
+        interleave();
+        mfma_block(buf, 3, acc1);
+        epilogue(acc0, 4 * tile + 2);
+        interleave();
         if (tile + 1 < n_tiles) store_tile(buf ^ 1);
         __syncthreads();
+        if (tile + 1 < n_tiles) mfma_block(buf ^ 1, 0, acc0);
+        epilogue(acc1, 4 * tile + 3);
     }
     if (!SAMPLE && lane < 8) {
         uint32_t c = 0;
@@ -749,6 +777,8 @@ size_t prefill_topk_workspace_bytes(int64_t T, int32_t ctx_len, int64_t q_pos0, 
 
 int prefill_topk_max_k() { return kKCap; }
 
+int64_t prefill_topk_max_cols() { return int64_t(1) << 24; }
+
 hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st) {
     if (L.T <= 0) return hipSuccess;
     PfArgs a;
@@ -783,6 +813,7 @@ hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st)
         if (cols > 0) {
             Geo gc = make_geo(cdiv(cols, kSub), qblocks, 4096 / kSub, kMaxKeysPerWG / kSub, n_cu);
             gc.cand_ld = w.cand_ld;
+            if (8 * 8 * w.cand_ld > 0x7fffffffLL) return hipErrorInvalidValue;
             gc.cnt_ld = w.cnt_ld;
             kpw = static_cast<int64_t>(gc.blocks) * kSub;
             score_mfma_kernel<false><<<grid_of(gc), 512, 0, st>>>(a, t0, t1, cols, gc, nullptr, 0, w.thr, w.counts,

@@ -304,8 +304,8 @@ int csa2_sparse_attn_prefill(const csa2_attn_prefill_args *a, void *ws, size_t w
  *   k_idx  one sequence's indexer cache, tiled layout (csa2_index_score),
  *          cap rows (cap % 64 == 0), bf16
  *   out_idx [T][k] int32: min(k, vis(t)) ascending positions, then -1.
- * 1 <= k <= 4096.  Inputs must be finite with scores far from float32
- * overflow.  Workspace: csa2_prefill_topk_workspace_size (about
+ * 1 <= k <= 4096 and vis(T-1) <= 2^24 (CSA2_E_UNSUPPORTED beyond).  Inputs
+ * must be finite with scores far from float32 overflow.  Workspace: csa2_prefill_topk_workspace_size (about
  * 4 * min(T, 1024) * vis(T-1) bytes of approximate scores plus 100 KB per
  * row of that chunk); 256-byte aligned.
  * ------------------------------------------------------------------------ */

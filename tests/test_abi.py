@@ -111,6 +111,10 @@ def test_prefill_topk_argument_checks():
     assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 1
     a.m, a.ctx_len = 2, 2000
     assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 1
+    a.cap, a.ctx_len, a.q_pos0, a.m = 1 << 25, 1 << 25, 1 << 25, 1     # 2^25 visible entries
+    assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 2
+    assert "visible entries" in _err()
+    a.cap, a.ctx_len, a.q_pos0, a.m = 1024, 2000, 1990, 2
     a.ctx_len, a.T = 1000, 0
     assert L.csa2_prefill_topk(ctypes.byref(a), None, 0, None) == 0    # nothing to do
 
