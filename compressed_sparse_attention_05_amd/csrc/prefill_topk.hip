@@ -445,11 +445,13 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
 // vis <= kCandCap take every visible key; otherwise L_t is the j-th largest
 // sampled s~, j = round(target * n_s / vis) with n_s visible sampled keys and
 // about target = min(3k, (k + kCandCap) / 2) keys expected at or above it.
-// The sample row is staged in LDS when it fits.
-constexpr int kSampLds = 16384;
+// A sample row of up to kSampReg keys is selected from registers (16 per
+// thread); longer rows are read from the workspace in radix passes.
+constexpr int kSampReg = 16384;
+constexpr int kSampPerThread = kSampReg / kThreads;
 __global__ __launch_bounds__(kThreads) void sample_thresh_kernel(int64_t t0, PfArgs a, const float* __restrict__ samp,
                                                                  int64_t ld_s, uint32_t* __restrict__ thr) {
-    __shared__ uint32_t sk[kSampLds];
+    __shared__ SelLds sh;
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t wave_tot[kWaves];
     __shared__ uint32_t res[2];
@@ -467,23 +469,35 @@ __global__ __launch_bounds__(kThreads) void sample_thresh_kernel(int64_t t0, PfA
     if (n > ld_s) n = ld_s;
     const float* s = samp + r * ld_s;
     const double target = fmin(3.0 * a.k, 0.5 * (a.k + kCandCap));
-    auto pick = [&](auto get) {
-        const uint32_t n_s = count_valid(get, n, wave_tot);
+    auto rank_of = [&](uint32_t n_s) {
         const double jd = target * static_cast<double>(n_s) / static_cast<double>(vis) + 0.5;
         uint32_t j = static_cast<uint32_t>(jd);
         if (j < 1u) j = 1u;
         if (j > n_s) j = n_s;
-        uint32_t T = 1u, need = 0;
-        if (n_s > 0) radix_select(get, n, j, hist, res, T, need);
-        if (threadIdx.x == 0) thr[r] = T > 0u ? T : 1u;
+        return j;
     };
-    if (n <= kSampLds) {
-        for (int64_t i = threadIdx.x; i < n; i += kThreads) sk[i] = key_of(s[i]);
-        __syncthreads();
-        pick([&](int64_t i) { return sk[i]; });
+    uint32_t T = 1u;
+    if (n <= kSampReg) {
+        // slot i = j * kThreads + tid (0 = empty past n)
+        uint32_t kk[kSampPerThread];
+#pragma unroll
+        for (int j = 0; j < kSampPerThread; ++j) {
+            const int64_t i = static_cast<int64_t>(j) * kThreads + threadIdx.x;
+            kk[j] = i < n ? key_of(s[i]) : 0u;
+        }
+        uint32_t mn, mx;
+        const uint32_t n_s = sel_stats<kSampPerThread>(kk, sh, mn, mx);
+        if (n_s > 0) {
+            uint32_t need = rank_of(n_s);
+            T = sel_passes<kSampPerThread, false>(kk, mn, mx, need, sh);
+        }
     } else {
-        pick([&](int64_t i) { return key_of(s[i]); });
+        auto get = [&](int64_t i) { return key_of(s[i]); };
+        const uint32_t n_s = count_valid(get, n, wave_tot);
+        uint32_t need = 0;
+        if (n_s > 0) radix_select(get, n, rank_of(n_s), hist, res, T, need);
     }
+    if (threadIdx.x == 0) thr[r] = T > 0u ? T : 1u;
 }
 
 // exact score of key row pos for query row t (q, w staged as float32 in LDS)
@@ -511,15 +525,51 @@ __device__ float exact_score(const float* qf, const float* wf, const uint8_t* kc
     return s;
 }
 
+// head h's channel chain of the same exact score: d_h with the channels in
+// order (exact_score keeps all heads in one thread; this splits them over 8
+// lanes, each chain unchanged)
+__device__ float exact_head(const float* qf, const uint8_t* kc, int64_t pos, int h) {
+    float d = 0.0f;
+    const float* qh = qf + h * kDim;
+#pragma unroll 4
+    for (int c = 0; c < kNch; ++c) {
+        const uint4 v = *kchunk(kc, pos, c);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ch = 8 * c + 2 * e;
+            d = fmaf(qh[ch], bf16_lo(u[e]), d);
+            d = fmaf(qh[ch + 1], bf16_hi(u[e]), d);
+        }
+    }
+    return d;
+}
+
+constexpr int kCandPerThread = kCandCap / kThreads;   // candidates held in registers during selection
+static_assert(kCandCap % kThreads == 0, "candidates split evenly over the threads");
+static_assert(sizeof(SelLds) <= 4 * kCandCap + 12 * kBandCap, "selection LDS fits over the keys and band arrays");
+
 __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs a, const float* __restrict__ eps,
                                                               const uint32_t* __restrict__ thr,
                                                               const uint32_t* __restrict__ counts, int64_t cnt_ld,
                                                               int64_t cand_ld, int64_t kpw,
                                                               uint2* __restrict__ cand_all,
                                                               int32_t* __restrict__ out) {
-    __shared__ uint2 cand[kCandCap];
-    __shared__ uint64_t band[kBandCap];
-    __shared__ uint32_t sel[kKCap];
+    // candidate keys (s~ bits, then order keys), band entries and band
+    // candidate indices; the selection's histograms take their place while
+    // the keys are held in registers.  Positions stay put.
+    __shared__ union CandLds {
+        struct {
+            uint32_t key[kCandCap];
+            uint64_t band[kBandCap];
+            uint32_t sel[kBandCap];
+        } c;
+        SelLds sh;
+    } u_lds;
+    __shared__ uint32_t cpos[kCandCap];
+    uint32_t* ckey = u_lds.c.key;
+    uint64_t* band = u_lds.c.band;
+    uint32_t* sel = u_lds.c.sel;
     __shared__ float qf[kHeads * kDim];
     __shared__ float wf[kHeads];
     __shared__ uint32_t hist[2048];
@@ -580,18 +630,38 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
             for (int s = wv; s < n_here; s += kWaves) {
                 const uint32_t so = hist[s], sc = hist[1024 + s];
                 const uint2* src = region + (sb + s) * kpw;
-                for (uint32_t i = lane; i < sc; i += 64) cand[so + i] = src[i];
+                for (uint32_t i = lane; i < sc; i += 64) {
+                    const uint2 cv = src[i];
+                    ckey[so + i] = cv.x;
+                    cpos[so + i] = cv.y;
+                }
             }
             running += tot;
             __syncthreads();
         }
-        // keys of s~ (candidates hold the float bits), in position order
-        for (uint32_t i = tid; i < C; i += kThreads) cand[i].x = key_of(__uint_as_float(cand[i].x));
+        // keys of s~ (candidates hold the float bits) into registers, slot
+        // i = j * kThreads + tid (0 = empty past C)
+        uint32_t kk[kCandPerThread];
+#pragma unroll
+        for (int j = 0; j < kCandPerThread; ++j) {
+            const uint32_t i = static_cast<uint32_t>(j * kThreads + tid);
+            kk[j] = i < C ? key_of(__uint_as_float(ckey[i])) : 0u;
+        }
         __syncthreads();
         // tau~: the k-th largest s~ (of the candidates, and of the row)
-        uint32_t T = 0, need = 0;
-        auto get = [&](int64_t i) { return cand[i].x; };
-        radix_select(get, C, k_eff, hist, res, T, need);
+        uint32_t T;
+        {
+            uint32_t mn, mx, need = k_eff;
+            sel_stats<kCandPerThread>(kk, u_lds.sh, mn, mx);
+            T = sel_passes<kCandPerThread, false>(kk, mn, mx, need, u_lds.sh);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kCandPerThread; ++j) {
+            const uint32_t i = static_cast<uint32_t>(j * kThreads + tid);
+            if (i < C) ckey[i] = kk[j];
+        }
+        __syncthreads();
         const float tau = float_of_key(T);
         const float e2 = 2.0f * eps[t];
         const uint32_t hi_key = key_of(next_up(tau + e2));
@@ -605,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
             // sure picks (s~ above the band) are counted; band keys go to
             // band[] as candidate indices
             for (uint32_t i = tid; i < C; i += kThreads) {
-                const uint32_t ck = cand[i].x;
+                const uint32_t ck = ckey[i];
                 if (ck > hi_key) {
                     atomicAdd(&counters[0], 1u);
                 } else if (ck >= lo_key) {
@@ -621,12 +691,24 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
                 // exact scores of the band keys, ranked by (score desc,
                 // position asc): entry = (~exact key << 32) | position, the
                 // need_b smallest entries are chosen
-                for (uint32_t i = tid; i < n_band; i += kThreads) {
+                // (8 lanes per band key, lane h%8 running head h's chain;
+                // the head sum is then taken in head order by the first)
+                for (uint32_t i = tid >> 3; i < n_band; i += kThreads / 8) {
                     const uint32_t ci = static_cast<uint32_t>(band[i]);
-                    const uint32_t pos = cand[ci].y;
-                    const uint32_t ek = key_of(exact_score(qf, wf, a.kc, pos));
-                    band[i] = (static_cast<uint64_t>(~ek) << 32) | pos;
-                    sel[i] = ci;
+                    const uint32_t pos = cpos[ci];
+                    const int h = tid & 7;
+                    const float d = exact_head(qf, a.kc, pos, h);
+                    float sc = 0.0f;
+#pragma unroll
+                    for (int hh = 0; hh < kHeads; ++hh) {
+                        const float dh = __shfl(d, (lane & ~7) + hh);
+                        sc = fmaf(wf[hh], dh > 0.0f ? dh : 0.0f, sc);
+                    }
+                    if (h == 0) {
+                        const uint32_t ek = key_of(sc);
+                        band[i] = (static_cast<uint64_t>(~ek) << 32) | pos;
+                        sel[i] = ci;
+                    }
                 }
                 __syncthreads();
                 const uint32_t need_b = k_eff - n_in;
@@ -637,17 +719,17 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
                     const uint64_t x = band[i];
                     uint32_t rank = 0;
                     for (uint32_t j2 = 0; j2 < n_band; ++j2) rank += band[j2] < x;
-                    if (rank < need_b) cand[sel[i]].x = 0xffffffffu;
+                    if (rank < need_b) ckey[sel[i]] = 0xffffffffu;
                 }
                 __syncthreads();
                 // ordered emission: candidates are in position order
                 uint32_t written = 0;
                 for (uint32_t base = 0; base < C; base += kThreads) {
                     const uint32_t i = base + tid;
-                    const bool pick = i < C && cand[i].x > hi_key;
+                    const bool pick = i < C && ckey[i] > hi_key;
                     uint32_t tot;
                     const uint32_t at = written + block_excl_prefix(pick, wave_tot, tot);
-                    if (pick && at < k_eff) o[at] = static_cast<int32_t>(cand[i].y);
+                    if (pick && at < k_eff) o[at] = static_cast<int32_t>(cpos[i]);
                     written += tot;
                 }
             }
