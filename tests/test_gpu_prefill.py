@@ -99,7 +99,7 @@ def test_prefill_topk_full_chunk_sampled(K):
 
 
 # Rows with more than 12,288 visible entries take the sampled threshold:
-# one 32-key block per 256 keys is scored first, the row's candidates are
+# one 32-key block per 512 keys is scored first, the row's candidates are
 # the keys at or above a sample quantile, and the final pass checks that
 # they cover the band around the k-th score.
 @pytest.mark.parametrize("k", [512, 2048])
@@ -113,7 +113,7 @@ def test_prefill_topk_sampled_threshold(K, k):
 
 
 def test_prefill_topk_sampled_ragged_context(K):
-    # ctx_len 20,000 is not a multiple of the 256-key sample group or of the
+    # ctx_len 20,000 is not a multiple of the 512-key sample group or of the
     # 4,096-key candidate workgroup: the last group and workgroup are partial
     T, cap, m, k = 40, 20480, 1, 1000
     ctx = 20000
@@ -121,6 +121,17 @@ def test_prefill_topk_sampled_ragged_context(K):
     q, w, kc = _inputs(2005, T, cap)
     got = _run(K, q, w, kc, ctx, q_pos0, m, k)
     _check_rows(got, q, w, kc, ctx, q_pos0, m, k, range(T))
+
+
+def test_prefill_topk_long_sample_row(K):
+    # 266,240 visible entries give 16,640 sampled keys per row, more than the
+    # threshold kernel holds in registers: it selects from the workspace
+    T, cap, m, k = 4, 266240, 1, 2048
+    q_pos0 = cap - T                  # vis(t) runs from cap - 3 to cap
+    q, w, kc = _inputs(2008, T, cap)
+    print(f"prefill topk long sample T={T} cap={cap} k={k}", flush=True)
+    got = _run(K, q, w, kc, cap, q_pos0, m, k)
+    _check_rows(got, q, w, kc, cap, q_pos0, m, k, range(T))
 
 
 def test_prefill_topk_too_many_candidates_falls_back(K):
