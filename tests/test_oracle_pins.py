@@ -632,3 +632,59 @@ def test_projection_chain_is_fused_and_forward():
     x[0, 1], W[1, 0] = 1.0, 1.0
     x[0, 2], W[2, 0] = 2.0 ** 30, -1.0
     assert oracle.project_kidx(x, W)[0, 0] == 0
+
+
+# ---------------------------------------------------------- prefill scores
+@pytest.mark.parametrize("m", [1, 2])
+def test_prefill_scores_equal_masked_float64_product(m):
+    """Per-row scores of a prefill chunk ("...KV Cache Compression" notes,
+    section 2: the encoder compresses m tokens per entry; section 3: a Full
+    layer scores every causally visible entry).
+
+    On an exactly-summable grid (q, k multiples of 2^-3 in [-4, 4], w multiples
+    of 2^-4) every partial sum is exact in float32, so the oracle's rows must
+    equal a float64 product masked by the closed-form visibility
+    vis(t) = min(ctx_len, floor((q_pos[t] + 1) / m)).  Non-square H_I x d_I,
+    per-row w and q, and ld > ctx_len catch a stride slip (row t reading row
+    t-1's q or w, or writing at t * ctx_len) and a visibility taken from the
+    wrong row (all rows see different counts here)."""
+    rng = np.random.default_rng(40 + m)
+    T, H_I, d_I, ctx, ld = 9, 3, 5, 37, 45
+    q = np.clip(np.round(rng.standard_normal((T, H_I, d_I)) * 8) / 8, -4, 4).astype(np.float32)
+    k = np.clip(np.round(rng.standard_normal((ctx, d_I)) * 8) / 8, -4, 4).astype(np.float32)
+    w = (rng.integers(1, 16, (T, H_I)) / 16).astype(np.float32)
+    # positions out of order and spread so every row has its own vis; the last
+    # row's count is capped by ctx_len
+    q_pos = np.array([0, 5, 2, 19, 11, 30, 33, 7, 200], np.int64)
+    got = oracle.prefill_scores(q, w, k, q_pos, ctx, m, ld)
+    assert got.shape == (T, ld)
+    seen = set()
+    for t in range(T):
+        vis = min(ctx, (int(q_pos[t]) + 1) // m)
+        seen.add(vis)
+        d = k.astype(np.float64) @ q[t].astype(np.float64).T        # [ctx][H_I]
+        ref = np.maximum(d, 0.0) @ w[t].astype(np.float64)           # [ctx]
+        assert np.array_equal(got[t, :vis].astype(np.float64), ref[:vis]), t
+        assert np.all(np.isneginf(got[t, vis:])), t
+    assert len(seen) == T          # every row has a different visible count
+    assert min(ctx, (200 + 1) // m) == ctx
+
+
+def test_prefill_scores_rows_are_independent_full_scores():
+    """Swapping two rows' (q, w, q_pos) swaps their output rows, and a row
+    equals the decode-form score of the same query over its visible entries:
+    a prefill row is a Full-layer score with its own visibility."""
+    rng = np.random.default_rng(77)
+    T, H_I, d_I, ctx = 4, 2, 7, 50
+    q = rng.standard_normal((T, H_I, d_I)).astype(np.float32)
+    k = rng.standard_normal((ctx, d_I)).astype(np.float32)
+    w = rng.random((T, H_I)).astype(np.float32)
+    q_pos = np.array([3, 60, 21, 98], np.int64)
+    a = oracle.prefill_scores(q, w, k, q_pos, ctx, 2, ctx)
+    perm = [2, 0, 3, 1]
+    b = oracle.prefill_scores(q[perm].copy(), w[perm].copy(), k, q_pos[perm].copy(), ctx, 2, ctx)
+    assert np.array_equal(a[perm].view(np.uint32), b.view(np.uint32))
+    for t in range(T):
+        vis = min(ctx, (int(q_pos[t]) + 1) // 2)
+        one = np.array([oracle.score_one(q[t], w[t], k[j]) for j in range(vis)], np.float32)
+        assert np.array_equal(a[t, :vis].view(np.uint32), one.view(np.uint32))
