@@ -195,6 +195,13 @@ class DecodeStep:
                 self.calls.append((f"score{li}", self.L.csa2_index_score,
                                    (ctypes.byref(sa), bd._ptr(ws), nws, None)))
                 fused = False
+                # The Full top-k may be taken inside a pool only when that pool
+                # was selected from this same layer's block maxima (the top-k
+                # lies inside its own layer's pool for k <= P_b).  A pool from
+                # another layer's scores, or one passed in, says nothing about
+                # this layer's scores, so a later Full layer selects over the
+                # whole visible context.
+                own_pool = False
                 if want_bm:
                     nb = (cap + 7) // 8
                     fused = k <= P_b <= 2048 and nb <= 32768
@@ -204,6 +211,7 @@ class DecodeStep:
                                        (bd._ptr(self.block_max), B, nb, nb, P_b, bd._ptr(self.pool),
                                         bd._ptr(self.scores), cap, k, bd._ptr(idx), None)))
                     pool_built = True
+                    own_pool = True
                 elif want_bm:
                     pws_n = self.L.csa2_build_candidate_pool_workspace_size(B, nb, P_b)
                     pws = torch.empty(max(pws_n, 256), dtype=torch.uint8, device=dev)
@@ -212,9 +220,10 @@ class DecodeStep:
                                        (bd._ptr(self.block_max), B, nb, nb, P_b,
                                         bd._ptr(self.pool), bd._ptr(pws), pws_n, None)))
                     pool_built = True
+                    own_pool = True
                 if fused:
                     pass
-                elif mode == "F" and pool_built and k <= P_b and 8 * P_b <= 32768:
+                elif mode == "F" and own_pool and k <= P_b and 8 * P_b <= 32768:
                     # the Full top-k lies inside the pool: select among its 8*P_b scores
                     self.calls.append((f"topk{li}", self.L.csa2_topk_from_pool,
                                        (bd._ptr(self.scores), B, cap, bd._ptr(self.pool), P_b, k,

@@ -41,7 +41,10 @@ class PrefillChunk:
                  ctx_len: int, q_pos0: int, m: int, k: int, W: int, layers: List[PrefillLayer], *,
                  new_kv: Optional[torch.Tensor] = None, new_kidx: Optional[torch.Tensor] = None,
                  dst_row: Optional[torch.Tensor] = None, swa_start: int = 0,
-                 sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
+                 sm_scale: Optional[float] = None, outs: Optional[List[torch.Tensor]] = None):
+        """outs: optional per-layer outputs, each [T][H][D] float32; every layer
+        writes its own (a Reuse layer attends with its own queries and window,
+        so its output differs from the Full layer's)."""
         if len(schedule) != len(layers) or not schedule or schedule[0] != "F" or set(schedule[1:]) - {"R"}:
             raise ValueError("an encoder chunk schedule is one Full layer then Reuse layers")
         cap, half = codes.shape
@@ -68,15 +71,23 @@ class PrefillChunk:
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
         self._keep += [pa, ws]
         self.calls.append(("topk", self.L.csa2_prefill_topk, (ctypes.byref(pa), bd._ptr(ws), nws, None)))
-        self.out = out if out is not None else torch.empty((T, layers[0].q.shape[1], D), dtype=torch.float32,
-                                                           device=dev)
+        if outs is not None and len(outs) != len(layers):
+            raise ValueError("outs needs one [T][H][D] tensor per layer")
+        self.outs = list(outs) if outs is not None else [
+            torch.empty((T, lay.q.shape[1], D), dtype=torch.float32, device=dev) for lay in layers]
+        for o, lay in zip(self.outs, layers):
+            if (o.dtype != torch.float32 or tuple(o.shape) != (T, lay.q.shape[1], D) or not o.is_contiguous()
+                    or o.device != dev):
+                raise ValueError("each layer output must be a contiguous float32 [T][H][D] tensor on the cache's device")
+        if len({o.data_ptr() for o in self.outs}) != len(self.outs):
+            raise ValueError("layer outputs must not share memory")
         scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(D)
         for li, lay in enumerate(layers):
             aa = bd.AttnPrefillArgs(q=lay.q.data_ptr(), q_dtype=bd._dtype(lay.q, "q"), codes=codes.data_ptr(),
                                     scales=scales.data_ptr(), cap=cap, idx=self.idx.data_ptr(), k=k,
                                     swa=lay.swa.data_ptr(), swa_dtype=bd._dtype(lay.swa, "swa"), W=W,
                                     q_pos0=int(q_pos0), swa_start=int(swa_start), T=T, H=lay.q.shape[1], D=D,
-                                    sm_scale=scale, out=self.out.data_ptr())
+                                    sm_scale=scale, out=self.outs[li].data_ptr())
             n = self.L.csa2_sparse_attn_prefill_workspace_size(ctypes.byref(aa))
             aws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
             self._keep += [aa, aws]
