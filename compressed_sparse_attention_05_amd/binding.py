@@ -83,6 +83,7 @@ SIGNATURES = {
     "csa2_decode_select": (ctypes.c_int, [ctypes.POINTER(DecodeSelectArgs), P, ctypes.c_size_t, P]),
     "csa2_sparse_attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), P, ctypes.c_size_t, P]),
+    "csa2_sparse_attn_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnArgs), P]),
     "csa2_sparse_attn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnPrefillArgs)]),
     "csa2_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(AttnPrefillArgs), P, ctypes.c_size_t, P]),
     "csa2_prefill_topk_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(PrefillTopkArgs)]),

@@ -5,10 +5,19 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/csa2.h"
 #include "csa2_internal.h"
+
+// Device scratch of csa2_sparse_attn_decode_noalloc: each GPU the library
+// runs on holds one copy, loaded with the code object, until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory;
+// the device address comes from hipGetSymbolAddress, taken once per device
+// (scratch_on_current_device) and used everywhere host code hands the array
+// to a kernel.
+static __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -40,6 +49,30 @@ size_t dtype_size(int dt) { return dt == CSA2_BF16 ? 2 : 4; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with that device current) and kept.
+int scratch_on_current_device(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CSA2_E_DEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CSA2_E_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(CSA2_E_DEVICE, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA2_OK;
+}
 
 }  // namespace
 
@@ -255,17 +288,34 @@ size_t csa2_sparse_attn_decode_workspace_size(const csa2_attn_args* a) {
     return csa2::attn_workspace_bytes(a->B, a->H, a->D, a->k, a->W);
 }
 
-int csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
-    if (!a) return fail(CSA2_E_INVALID, "csa2_sparse_attn_decode: args is null");
-    int rc = check_attn_common("csa2_sparse_attn_decode", a->q, a->q_dtype, a->codes, a->scales, a->cap,
+// Shared by csa2_sparse_attn_decode (caller's workspace) and
+// csa2_sparse_attn_decode_noalloc (the library's device scratch).
+static int attn_decode_checked(const char* fn, const csa2_attn_args* a, void* ws, size_t ws_bytes,
+                               bool use_scratch, void* stream) {
+    if (!a) return fail(CSA2_E_INVALID, "%s: args is null", fn);
+    int rc = check_attn_common(fn, a->q, a->q_dtype, a->codes, a->scales, a->cap,
                                a->idx, a->k, a->swa, a->swa_dtype, a->W, a->B, a->H, a->D, a->out);
     if (rc != CSA2_OK) return rc;
     if (a->B == 0) return ok();
-    if (a->W > 0 && !a->swa_len) return fail(CSA2_E_INVALID, "csa2_sparse_attn_decode: swa_len is null");
+    if (a->W > 0 && !a->swa_len) return fail(CSA2_E_INVALID, "%s: swa_len is null", fn);
     const size_t need = csa2_sparse_attn_decode_workspace_size(a);
+    if (use_scratch) {
+        if (need > CSA2_NOALLOC_SCRATCH_BYTES)
+            return fail(CSA2_E_WORKSPACE,
+                        "%s: this call needs %zu bytes of scratch, more than the %zu the library holds per "
+                        "device; use csa2_sparse_attn_decode with a workspace",
+                        fn, need, static_cast<size_t>(CSA2_NOALLOC_SCRATCH_BYTES));
+        ws = nullptr;
+        ws_bytes = 0;
+        if (need > 0) {
+            rc = scratch_on_current_device(fn, &ws);
+            if (rc != CSA2_OK) return rc;
+            ws_bytes = CSA2_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     if (need > 0 && (!ws || ws_bytes < need))
-        return fail(CSA2_E_WORKSPACE, "csa2_sparse_attn_decode: workspace %zu bytes < required %zu", ws_bytes, need);
-    if (ws && !aligned(ws, 16)) return fail(CSA2_E_INVALID, "csa2_sparse_attn_decode: workspace must be 16-byte aligned");
+        return fail(CSA2_E_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (ws && !aligned(ws, 16)) return fail(CSA2_E_INVALID, "%s: workspace must be 16-byte aligned", fn);
     csa2::AttnLaunch L;
     L.q = a->q; L.q_bf16 = a->q_dtype == CSA2_BF16;
     L.codes = a->codes; L.scales = a->scales; L.cap = a->cap; L.kv_unit_stride = a->cap;
@@ -274,7 +324,15 @@ int csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_bytes, 
     L.q_pos0 = 0; L.swa_start = 0; L.prefill = false;
     L.units = a->B; L.H = a->H; L.D = a->D; L.sm_scale = a->sm_scale; L.out = a->out;
     L.ws = need > 0 ? static_cast<float*>(ws) : nullptr; L.ws_bytes = ws_bytes;
-    return device_status(csa2::launch_attn(L, as_stream(stream)), "csa2_sparse_attn_decode");
+    return device_status(csa2::launch_attn(L, as_stream(stream)), fn);
+}
+
+int csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+    return attn_decode_checked("csa2_sparse_attn_decode", a, ws, ws_bytes, false, stream);
+}
+
+int csa2_sparse_attn_decode_noalloc(const csa2_attn_args* a, void* stream) {
+    return attn_decode_checked("csa2_sparse_attn_decode_noalloc", a, nullptr, 0, true, stream);
 }
 
 size_t csa2_sparse_attn_prefill_workspace_size(const csa2_attn_prefill_args* a) {

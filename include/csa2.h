@@ -263,6 +263,26 @@ size_t csa2_sparse_attn_decode_workspace_size(const csa2_attn_args *a);
 int csa2_sparse_attn_decode(const csa2_attn_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * csa2_sparse_attn_decode_noalloc - csa2_sparse_attn_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and outputs as
+ * csa2_sparse_attn_decode; the key-split partials go to a scratch array of
+ * CSA2_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * copy per GPU, from the first call on that GPU until the process ends.
+ * The call allocates nothing and calls no allocating routine.
+ * Calls whose workspace (csa2_sparse_attn_decode_workspace_size) exceeds
+ * CSA2_NOALLOC_SCRATCH_BYTES return CSA2_E_WORKSPACE and enqueue nothing.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (on different streams, or from different host threads
+ * without ordering) race and give wrong results.  Calls ordered on one
+ * stream are safe.  The scratch keeps the last call's partials; nothing in
+ * it needs to start at zero.
+ * ------------------------------------------------------------------------ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int csa2_sparse_attn_decode_noalloc(const csa2_attn_args *a, void *stream);
+
+/* ------------------------------------------------------------------------
  * csa2_sparse_attn_prefill - the same per query token of one sequence's
  * chunk.  Query t sits at token position i = q_pos0 + t and uses its own
  * idx[t] row plus the window [max(swa_start, i - W + 1), i] ([KVC] section

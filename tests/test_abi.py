@@ -189,3 +189,19 @@ def test_mhc_step_rejects_bad_arguments_on_host():
     assert L.csa2_mhc_step(ctypes.byref(a), None) == 1 and "null" in _err()
     a.T = 0
     assert L.csa2_mhc_step(ctypes.byref(a), None) == 0
+
+
+def test_noalloc_attention_rejects_calls_beyond_its_scratch_on_host():
+    L = binding.lib()
+    a = binding.AttnArgs(q=16, q_dtype=1, codes=16, scales=16, cap=1 << 20, idx=16, k=2048, swa=16,
+                         swa_dtype=1, W=128, swa_len=16, B=1408, H=64, D=512, sm_scale=0.1, out=16)
+    need = L.csa2_sparse_attn_decode_workspace_size(ctypes.byref(a))
+    limit = 64 << 20
+    assert need > limit
+    assert L.csa2_sparse_attn_decode_noalloc(ctypes.byref(a), None) == 3
+    assert "scratch" in _err() and str(limit) in _err()
+    a.H = 48
+    assert L.csa2_sparse_attn_decode_noalloc(ctypes.byref(a), None) == 2
+    assert L.csa2_sparse_attn_decode_noalloc(None, None) == 1
+    a.H, a.B = 64, 0
+    assert L.csa2_sparse_attn_decode_noalloc(ctypes.byref(a), None) == 0    # nothing to do
