@@ -521,9 +521,18 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
 //            and issue the gathers of tile i + 2
 // so the matrix cores of every SIMD get work from both roles and no S
 // partial sums cross waves (each S-wave covers all channels).  The gathers
-// are buffer loads whose row offset is a scalar, so a key costs no vector
-// address arithmetic; rows beyond the cache read zeros.
-template <bool BF16>
+// are buffer loads whose row offset is a plain integer (rows beyond the
+// cache read zeros); one load path per instantiation, since a branch between
+// buffer and global loads makes the compiler wait for every gather where the
+// paths join.
+// Start-up: the first tile's gathers go out first (index entries straight
+// from global memory), then the unit's q is read once by all 512 threads in
+// 1 KiB runs and staged in the second Kt buffer, from which each S-wave
+// takes its fragments.  A split's generic tiles (window rows, or a tile
+// straddling the main/window boundary) come first, the first of them loaded
+// during start-up; the online softmax does not depend on the order beyond
+// rounding.
+template <bool BF16, bool USE_BUF>
 __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     constexpr int D = 512, KT = 64, KROW = D + 8, SSTEPS = D / 16;
     __shared__ __attribute__((aligned(16))) _Float16 Kt[2][KT * KROW];
@@ -571,89 +580,34 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     if (t_end > a.n_tiles) t_end = a.n_tiles;
     const int n_it = t_end > t_begin ? t_end - t_begin : 0;
     const int t_main_end = a.k / KT;        // tiles made only of main-KV slots
+    // iteration order: generic tiles first, then main tiles t_begin, ...
+    const int t_first_gen = t_begin > t_main_end ? t_begin : t_main_end;
+    const int n_gen = t_end > t_first_gen ? t_end - t_first_gen : 0;
+    auto tile_of = [&](int it) { return it < n_gen ? t_first_gen + it : t_begin + (it - n_gen); };
+    auto is_main = [&](int it) { return it >= n_gen; };
 
-    int win0 = t_begin;
-    auto stage_idx = [&](int first_tile) {
-        win0 = first_tile;
-        for (int i = tid; i < kMaxTilesPerSplit * KT; i += 512) {
-            const int slot = first_tile * KT + i;
-            idx_s[i] = slot < a.k ? idx[slot] : -1;
-        }
-    };
-    stage_idx(t_begin);
-
-    // ---- role registers: R holds the q fragments of an S-wave (32 k-steps
-    // x 4 dwords) or the O^T accumulators of a D-wave (4 d tiles x 2 head
-    // tiles); a wave keeps one role for the whole kernel, so the two share
-    // the same 128 registers
-    floatx16 R[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) R[i][r] = 0.0f;
-    auto qfrag = [&](int st) {
-        const int b = 4 * (st & 3);
-        return __builtin_bit_cast(half8, make_float4(R[st >> 2][b], R[st >> 2][b + 1], R[st >> 2][b + 2],
-                                                     R[st >> 2][b + 3]));
-    };
-    float m_run = -__builtin_inff(), l_run = 0.0f;
-    if (s_role) {
-        // H is a multiple of 64 at D = 512, so every head of the block exists
-        const int head = hbase + 32 * hg + (lane & 31);
-        const int64_t qrow = (u * a.H + head) * D;
-#pragma unroll
-        for (int st = 0; st < SSTEPS; ++st) {
-            const int d0 = 16 * st + 8 * (lane >> 5);
-            uint32_t wd[4];
-            if (BF16) {
-                const uint4 r = *reinterpret_cast<const uint4*>(a.q + qrow + d0);
-                const uint32_t in[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    wd[e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
-            } else {
-                const float* q32 = reinterpret_cast<const float*>(a.q) + qrow + d0;
-                const uint4 r0 = *reinterpret_cast<const uint4*>(q32);
-                const uint4 r1 = *reinterpret_cast<const uint4*>(q32 + 4);
-                wd[0] = pack_h2(__uint_as_float(r0.x), __uint_as_float(r0.y));
-                wd[1] = pack_h2(__uint_as_float(r0.z), __uint_as_float(r0.w));
-                wd[2] = pack_h2(__uint_as_float(r1.x), __uint_as_float(r1.y));
-                wd[3] = pack_h2(__uint_as_float(r1.z), __uint_as_float(r1.w));
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) R[st >> 2][4 * (st & 3) + e] = __uint_as_float(wd[e]);
-        }
-    }
-
-    // ---- D-wave state: O^T accumulator (d tile mt, head tile nt) is
-    // R[2mt + nt].  Every wave gathers 8 keys (8w .. 8w + 7) of the next main
-    // tile in two groups of 4: lane l takes key 4g + l/16 of the group and
-    // its channels 32(l%16) .. +31 (16 code bytes and 2 scale bytes), so a
-    // group is one 16-byte load and one 2-byte load per lane.
+    // ---- gathers: lane l takes key 4g + l / 16 of this wave's group g and
+    // its channels 32(l % 16) .. + 31 (16 code bytes, 2 scale bytes), so a
+    // group is one 16-byte load and one 2-byte load per lane
     constexpr int KPW = KT / 8;                       // keys gathered per wave
     uint4 pm_c[2];
     uint32_t pm_s[2];
     uint32_t pm_ok = 0;                               // bit g: this lane's key of group g is a real row
-    // buffer resources over this unit's rows (offsets fit 32 bits when the
-    // cache has fewer than 2^31 / 256 rows; larger caches use global loads)
-    const bool use_buf = a.cap * (D / 2) <= 0x7fffffffLL;
     const __amdgpu_buffer_rsrc_t rc_codes = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.codes + kvbase * (D / 2)), static_cast<short>(0),
-        use_buf ? static_cast<int>(a.cap * (D / 2)) : 0, 0x00020000);
+        USE_BUF ? static_cast<int>(a.cap * (D / 2)) : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rc_scales = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.scales + kvbase * (D / 16)), static_cast<short>(0),
-        use_buf ? static_cast<int>(a.cap * (D / 16)) : 0, 0x00020000);
+        USE_BUF ? static_cast<int>(a.cap * (D / 16)) : 0, 0x00020000);
     const int gpart = lane & 15, gkey = lane >> 4;
-    auto prefetch_main = [&](int tile) {
+    auto gather_rows = [&](const int32_t (&row)[2]) {
         pm_ok = 0;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            const int key = KPW * wv + 4 * g + gkey;
-            const int32_t row = idx_s[tile * KT + key - win0 * KT];
-            const bool ok = row >= 0 && row < a.cap;
-            const int32_t rw = ok ? row : 0;
+            const bool ok = row[g] >= 0 && row[g] < a.cap;
+            const int32_t rw = ok ? row[g] : 0;
             pm_ok |= ok ? (1u << g) : 0u;
-            if (use_buf) {
+            if constexpr (USE_BUF) {
                 pm_c[g] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         rc_codes, rw * (D / 2) + 16 * gpart, 0, 0));
                 pm_s[g] = __builtin_amdgcn_raw_buffer_load_b16(rc_scales, rw * (D / 16) + 2 * gpart, 0, 0);
@@ -663,6 +617,21 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
                 pm_s[g] = *reinterpret_cast<const uint16_t*>(a.scales + rr * (D / 16) + 2 * gpart);
             }
         }
+    };
+    int win0 = t_begin;
+    auto stage_idx = [&](int first_tile) {
+        win0 = first_tile;
+        for (int i = tid; i < kMaxTilesPerSplit * KT; i += 512) {
+            const int slot = first_tile * KT + i;
+            idx_s[i] = slot < a.k ? idx[slot] : -1;
+        }
+    };
+    // main tile `tile`: index entries from the staged window
+    auto prefetch_main = [&](int tile) {
+        int32_t row[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) row[g] = idx_s[tile * KT + KPW * wv + 4 * g + gkey - win0 * KT];
+        gather_rows(row);
     };
     // one key row (all lanes, 8 channels each); every lane writes the mask
     // entry (the same value), so the write needs no branch
@@ -690,7 +659,8 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             kmask[buf][key] = ((pm_ok >> g) & 1u) ? 0.0f : -__builtin_inff();
         }
     };
-    // any tile (main rows, window rows, empty slots), loaded and stored at once
+    // any tile (main rows, window rows, empty slots), loaded and stored at
+    // once; index entries straight from global memory
     auto load_generic = [&](int tile, int buf) {
         for (int i = 0; i < KPW; ++i) {
             const int key = KPW * wv + i;
@@ -698,7 +668,7 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             uint32_t h[4] = {0u, 0u, 0u, 0u};
             bool valid = false;
             if (slot < a.k) {
-                const int32_t row = __builtin_amdgcn_readfirstlane(idx_s[slot - win0 * KT]);
+                const int32_t row = __builtin_amdgcn_readfirstlane(idx[slot]);
                 valid = row >= 0 && row < a.cap;
                 const int64_t rr = kvbase + (valid ? row : 0);
                 const uint32_t cw = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * lane);
@@ -725,6 +695,92 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             store_key(buf, key, h, valid);
         }
     };
+
+    // ---- start-up.  First gathers (index entries from global memory),
+    // then the index window, then q.
+    if (n_it > 0 && is_main(0)) {
+        int32_t row[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int slot = tile_of(0) * KT + KPW * wv + 4 * g + gkey;
+            row[g] = slot < a.k ? idx[slot] : -1;
+        }
+        gather_rows(row);
+    }
+    stage_idx(t_begin);
+    // q[u][hbase .. hbase + 63][0 .. 511] read once by all threads in 1 KiB
+    // runs (thread t: 16-byte pieces t, t + 512, ...), staged as fp16 rows
+    // of Kt[1] (the second tile buffer is free until phase 2 of the first
+    // tile)
+    {
+        constexpr int QCH = 64 * D / 8;                    // 16-byte (bf16) or 32-byte (fp32) pieces
+        const int64_t qbase = (u * a.H + hbase) * static_cast<int64_t>(D);
+        uint32_t qh[QCH / 512][4];
+#pragma unroll
+        for (int r = 0; r < QCH / 512; ++r) {
+            const int c = tid + 512 * r;                   // piece: head c / 64, channels 8 (c % 64) ..
+            if (BF16) {
+                const uint4 v = *reinterpret_cast<const uint4*>(a.q + qbase + 8 * static_cast<int64_t>(c));
+                qh[r][0] = v.x; qh[r][1] = v.y; qh[r][2] = v.z; qh[r][3] = v.w;
+            } else {
+                const float* q32 = reinterpret_cast<const float*>(a.q) + qbase + 8 * static_cast<int64_t>(c);
+                const uint4 v0 = *reinterpret_cast<const uint4*>(q32);
+                const uint4 v1 = *reinterpret_cast<const uint4*>(q32 + 4);
+                qh[r][0] = pack_h2(__uint_as_float(v0.x), __uint_as_float(v0.y));
+                qh[r][1] = pack_h2(__uint_as_float(v0.z), __uint_as_float(v0.w));
+                qh[r][2] = pack_h2(__uint_as_float(v1.x), __uint_as_float(v1.y));
+                qh[r][3] = pack_h2(__uint_as_float(v1.z), __uint_as_float(v1.w));
+            }
+        }
+        // the first tile, when it is a generic one, while q is in flight
+        if (n_it > 0 && !is_main(0)) load_generic(tile_of(0), 0);
+#pragma unroll
+        for (int r = 0; r < QCH / 512; ++r) {
+            const int c = tid + 512 * r;
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = BF16 ? pack_h2(__uint_as_float(qh[r][e] << 16), __uint_as_float(qh[r][e] & 0xffff0000u))
+                            : qh[r][e];
+            *reinterpret_cast<uint4*>(&Kt[1][(c >> 6) * KROW + 8 * (c & 63)]) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    if (tid < 2) grow_s[tid] = 0;
+    __syncthreads();                                  // idx_s and q staged
+
+    // ---- role registers: R holds the q fragments of an S-wave (32 k-steps
+    // x 4 dwords) or the O^T accumulators of a D-wave (4 d tiles x 2 head
+    // tiles); a wave keeps one role for the whole kernel, so the two share
+    // the same 128 registers
+    floatx16 R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) R[i][r] = 0.0f;
+    auto qfrag = [&](int st) {
+        const int b = 4 * (st & 3);
+        return __builtin_bit_cast(half8, make_float4(R[st >> 2][b], R[st >> 2][b + 1], R[st >> 2][b + 2],
+                                                     R[st >> 2][b + 3]));
+    };
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+    if (s_role) {
+        // head 32hg + lane % 32 of the block, channels 16st + 8(lane / 32) ..
+        const _Float16* qrow = &Kt[1][(32 * hg + (lane & 31)) * KROW + 8 * (lane >> 5)];
+#pragma unroll
+        for (int st = 0; st < SSTEPS; ++st) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * st);
+            R[st >> 2][4 * (st & 3)] = __uint_as_float(v.x);
+            R[st >> 2][4 * (st & 3) + 1] = __uint_as_float(v.y);
+            R[st >> 2][4 * (st & 3) + 2] = __uint_as_float(v.z);
+            R[st >> 2][4 * (st & 3) + 3] = __uint_as_float(v.w);
+        }
+    }
+    if (n_it > 0) {
+        if (is_main(0)) dequant_prefetched(0);
+        if (n_it > 1 && is_main(1)) prefetch_main(tile_of(1));
+    }
+    __syncthreads();                                  // first tile in Kt[0], q taken
+
     // O^T += V^T P^T for the tile in Kt[buf] with the P fragments in Pb
     auto pv_tile = [&](int buf) {
         if (grow_s[0] | grow_s[1]) {
@@ -763,21 +819,8 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
         }
     };
 
-    if (tid < 2) grow_s[tid] = 0;
-    __syncthreads();                                  // idx_s staged
-    if (n_it > 0) {
-        if (t_begin < t_main_end) {
-            prefetch_main(t_begin);
-            dequant_prefetched(0);
-        } else {
-            load_generic(t_begin, 0);
-        }
-        if (t_begin + 1 < t_end && t_begin + 1 < t_main_end) prefetch_main(t_begin + 1);
-    }
-    __syncthreads();
-
     for (int it = 0; it < n_it; ++it) {
-        const int tile = t_begin + it, buf = it & 1;
+        const int buf = it & 1;
         // ---------------- phase 1
         float t2[16];
         if (s_role) {
@@ -817,8 +860,9 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
         }
         __syncthreads();
         // ---------------- phase 2
-        if (it + 2 < n_it && tile + 2 - win0 >= kMaxTilesPerSplit) {
-            stage_idx(tile + 1);
+        // index window for the main tile gathered at the end of this phase
+        if (it + 2 < n_it && is_main(it + 2) && tile_of(it + 2) - win0 >= kMaxTilesPerSplit) {
+            stage_idx(tile_of(it + 2));
             __syncthreads();
         }
         if (s_role) {
@@ -857,10 +901,10 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             Pb[hg][2 * kb][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
             Pb[hg][2 * kb + 1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
         }
-        if (tile + 1 < t_end) {
-            if (tile + 1 < t_main_end) dequant_prefetched(buf ^ 1);
-            else load_generic(tile + 1, buf ^ 1);
-            if (tile + 2 < t_end && tile + 2 < t_main_end) prefetch_main(tile + 2);
+        if (it + 1 < n_it) {
+            if (is_main(it + 1)) dequant_prefetched(buf ^ 1);
+            else load_generic(tile_of(it + 1), buf ^ 1);
+            if (it + 2 < n_it && is_main(it + 2)) prefetch_main(tile_of(it + 2));
         }
         __syncthreads();
     }
@@ -1115,8 +1159,13 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     // heads, k = 2048: 28.8 against 42.0 us at 16 units, 39.4 against 56.4 us
     // at 32); at 8 units the split kernel's shorter start-up wins (23.4
     // against 24.7 us)
-    if (use_ws(L.units, D))
-        attn_ws_kernel<BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 512, 0, st>>>(a);
+    if (use_ws(L.units, D)) {
+        const dim3 grid(static_cast<unsigned>(L.units), sp.splits, hblocks);
+        if (L.cap * (D / 2) <= 0x7fffffffLL)
+            attn_ws_kernel<BF16, true><<<grid, 512, 0, st>>>(a);
+        else
+            attn_ws_kernel<BF16, false><<<grid, 512, 0, st>>>(a);
+    }
     else
         attn_kernel<D, NQ, BF16><<<dim3(static_cast<unsigned>(L.units), sp.splits, hblocks), 128 * NQ, 0, st>>>(a);
     hipError_t e = hipGetLastError();
