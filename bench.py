@@ -426,52 +426,81 @@ def run_mhc(K, dev, reps: int = 20, T: int = 8192, d: int = 4096):
             "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
     """The oracle, as it stands, on n_queries sequences of the workload's
-    first Full layer (write + scan + block max + pool + top-k + attention).
-    Sequences are independent, so they run on parallel host threads (the
-    oracle's C calls release the GIL); each sequence's arithmetic is the
-    oracle's single-threaded code.  The timed passes repeat until they hold
-    about 10 s of CPU work (wall time x threads; at least 3 passes), so the
-    rate is not one short sample.  Returns (queries/s, seconds, threads,
-    passes)."""
+    first Full layer (write + scan + block max + pool + top-k + attention),
+    on every host core available to this process.
+
+    The work is cut into units that the oracle computes independently: the
+    scan of a sequence in fixed position ranges (each score is its own fma
+    chain, so the ranges reproduce the whole row bit for bit), the block max,
+    pool and top-k of a sequence, and its attention in fixed head ranges
+    (each head is computed on its own).  Units run on a thread pool (the
+    oracle's C calls release the GIL).  The timed passes repeat until they
+    hold about 10 s of CPU work (wall time x threads; at least 3 passes).
+    A single-thread figure (one sequence, every unit on one thread) is taken
+    as well.  Returns a dict."""
     from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
     import compressed_sparse_attention_05_amd as K
 
-    B, N, D = w.B, w.N, w.D
+    B, N, D, H = w.B, w.N, w.D, w.H
     lay = s.layers[0]
-    threads = max(1, min(n_queries, len(os.sched_getaffinity(0))))
+    cores = len(os.sched_getaffinity(0))
+    threads = max(1, cores)
     oracle.lib()
     seqs = []
     for b in range(n_queries):
         kc_f = oracle.as_f32(K.untile_indexer_cache(s.k_idx[b:b + 1])[0].cpu())   # generator output
         kc_f[N - 1] = oracle.as_f32(s.new_kidx[b:b + 1].cpu())[0]
-        seqs.append(dict(kc=kc_f, qi=lay.q_idx[b, 0].cpu(), wt=lay.w[b, 0].cpu(), q=lay.q[b].cpu(),
-                         swa=lay.swa[b].cpu(), new_kv=s.new_kv[b:b + 1].cpu()))
+        seqs.append(dict(kc=kc_f, qi=lay.q_idx[b, 0].cpu(), wt=lay.w[b, 0].cpu(), q=oracle.as_f32(lay.q[b]),
+                         swa=lay.swa[b].cpu(), new_kv=s.new_kv[b:b + 1].cpu(),
+                         sc=np.empty(N, np.float32), out=np.empty((H, D), np.float32)))
+    # scan ranges: enough units for every thread, in whole 8-position blocks
+    per_seq = max(1, -(-2 * threads // n_queries))
+    step_rows = -(-N // per_seq)
+    step_rows = -(-step_rows // 8) * 8
+    ranges = [(r0, min(N, r0 + step_rows)) for r0 in range(0, N, step_rows)]
+    heads_per = max(1, H // max(1, -(-2 * threads // n_queries)))
+    hranges = [(h0, min(H, h0 + heads_per)) for h0 in range(0, H, heads_per)]
+
+    def scan(unit):
+        d, r0, r1 = unit
+        d["sc"][r0:r1] = oracle.full_scores(d["qi"], d["wt"], d["kc"][r0:r1], r1 - r0, r1 - r0)
 
     def select(d):
         oracle.mxfp4_encode(d["new_kv"])
-        sc = oracle.full_scores(d["qi"], d["wt"], d["kc"], N, N)
-        bm = oracle.block_max(sc, N, (N + 7) // 8)
+        bm = oracle.block_max(d["sc"], N, (N + 7) // 8)
         oracle.candidate_pool(bm, w.P_b)
-        d["idx"] = oracle.topk(sc, w.k)
+        d["idx"] = oracle.topk(d["sc"], w.k)
 
-    def attend(d):
-        oracle.attn_decode(d["q"], d["codes"], d["scales"], d["idx"], d["swa"], w.W, 1.0 / math.sqrt(D))
+    def attend(unit):
+        d, h0, h1 = unit
+        d["out"][h0:h1] = oracle.attn_decode(d["q"][h0:h1], d["codes"], d["scales"], d["idx"], d["swa"], w.W,
+                                             1.0 / math.sqrt(D))
 
-    with ThreadPoolExecutor(threads) as ex:
-        t0 = time.perf_counter()
-        list(ex.map(select, seqs))
-        t_sel = time.perf_counter() - t0
+    scan_units = [(d, r0, r1) for d in seqs for r0, r1 in ranges]
+    attn_units = [(d, h0, h1) for d in seqs for h0, h1 in hranges]
+
+    def prepare_rows():
         # the cache rows the attention reads, encoded by the oracle from the
         # generator (the cache existed before this step; untimed)
         for b, d in enumerate(seqs):
             idx = d["idx"]
             sel = torch.from_numpy(idx[idx >= 0].astype(np.int64))
-            raw = ci.gaussian_rows(s.seed, ci.TID_KV, b * N + sel, D, dtype=torch.bfloat16,
-                                   clip=ci.NORM_BOUND)
+            raw = ci.gaussian_rows(s.seed, ci.TID_KV, b * N + sel, D, dtype=torch.bfloat16, clip=ci.NORM_BOUND)
             codes = np.zeros((N, D // 2), np.uint8)
             scales = np.zeros((N, D // 16), np.uint8)
             c, sc_ = oracle.mxfp4_encode(raw)
@@ -480,21 +509,33 @@ def cpu_baseline(w: ci.Workload, s: InputSet, n_queries: int):
                 c1, s1 = oracle.mxfp4_encode(d["new_kv"])
                 codes[N - 1], scales[N - 1] = c1[0], s1[0]
             d["codes"], d["scales"] = codes, scales
+
+    def one_pass(ex):
         t0 = time.perf_counter()
-        list(ex.map(attend, seqs))
-        t_att = time.perf_counter() - t0
-        # further passes of the same work (each rewrites what the first did)
+        list(ex.map(scan, scan_units))
+        list(ex.map(select, seqs))
+        t1 = time.perf_counter()
+        if "codes" not in seqs[0]:
+            prepare_rows()
+        t2 = time.perf_counter()
+        list(ex.map(attend, attn_units))
+        return (t1 - t0) + (time.perf_counter() - t2)
+
+    with ThreadPoolExecutor(threads) as ex:
+        secs = one_pass(ex)
         passes = 1
-        while passes < 3 or ((t_sel + t_att) * threads < 10.0 and passes < 64):
-            t0 = time.perf_counter()
-            list(ex.map(select, seqs))
-            t_sel += time.perf_counter() - t0
-            t0 = time.perf_counter()
-            list(ex.map(attend, seqs))
-            t_att += time.perf_counter() - t0
+        while passes < 3 or (secs * threads < 10.0 and passes < 64):
+            secs += one_pass(ex)
             passes += 1
-    secs = t_sel + t_att
-    return passes * n_queries / secs, secs, threads, passes
+    # one thread, one sequence
+    d0 = seqs[0]
+    t0 = time.perf_counter()
+    scan((d0, 0, N))
+    select(d0)
+    attend((d0, 0, H))
+    t_one = time.perf_counter() - t0
+    return {"value": passes * n_queries / secs, "secs": secs, "threads": threads, "passes": passes,
+            "units": (len(scan_units), len(attn_units)), "one_thread_value": 1.0 / t_one}
 
 
 def calibrate_copy(mib: int, reps: int, dev):
@@ -582,7 +623,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 scores and softmax; f16 MFMA with f32 accumulation for attention",
         "data": "synthetic (seeded counter-based Gaussian/uniform; MXFP4 KV, bf16 indexer K, Q, SWA)",
         "config": {"workload": w.name, "batch": w.B, "context": w.N, "schedule": w.schedule,
                    "top_k": w.k, "window": w.W, "heads": w.H, "latent": w.D,
@@ -603,12 +644,16 @@ def main(argv=None):
     if args.cpu_queries > 0:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         nq = min(args.cpu_queries, w.B)
-        cps, secs, threads, passes = cpu_baseline(w, r["sets"][0], nq)
+        cb = cpu_baseline(w, r["sets"][0], nq)
         result["cpu_baseline"] = {
-            "value": round(cps, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "value": round(cb["value"], 4), "unit": "queries/s", "cores": cb["threads"], "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "one_thread_value": round(cb["one_thread_value"], 4),
             "sample": f"{nq} of {w.B} sequences of {w.name} (full work each: write, "
                       f"scan of {w.N} entries, block max, pool, top-{w.k}, attention), "
-                      f"{passes} passes, {secs:.2f} s wall on {threads} threads, one sequence per thread",
+                      f"{cb['passes']} passes, {cb['secs']:.2f} s wall on {cb['threads']} threads "
+                      f"(all cores available to the process); units: {cb['units'][0]} scan ranges and "
+                      f"{cb['units'][1]} attention head ranges; one_thread_value: one sequence on one thread",
         }
     if args.secondary:
         sec = []

@@ -193,8 +193,12 @@ struct Geo {
     int64_t cand_ld;     // candidate slots per row
     int64_t cnt_ld;      // count entries per row
 };
+// the top kSampBits bits of a multiplicative hash of the group index pick
+// one of its kGroup / kSub blocks, so every block of a group can be sampled
+constexpr int kSampBits = 4;
+static_assert(kGroup / kSub == (1 << kSampBits), "the sample hash must cover every block of a group");
 __device__ __forceinline__ int sample_block(int64_t group) {
-    return static_cast<int>((static_cast<uint32_t>(group) * 0x9E3779B1u) >> 29) & (kGroup / kSub - 1);
+    return static_cast<int>((static_cast<uint32_t>(group) * 0x9E3779B1u) >> (32 - kSampBits));
 }
 
 // float threshold of a row's candidate key: 1 -> -inf (every visible key),
