@@ -173,8 +173,11 @@ def algorithmic_bytes_per_query(w: ci.Workload):
 
 def scan_bytes_per_launch(w: ci.Workload):
     """Full scan (dominant kernel): indexer-K rows of every visible entry plus
-    the indexer queries and head weights, for the B rows of one launch."""
-    return w.B * (w.N * w.d_I * 2 + w.H_I * w.d_I * 2 + w.H_I * 4)
+    the indexer queries and head weights, for the B rows of one launch; the
+    launch also writes the token's entry (bf16 latent row and indexer key
+    read, MXFP4 row and key written)."""
+    write = w.D * 2 + w.d_I * 2 + w.D // 2 + w.D // 16 + w.d_I * 2
+    return w.B * (w.N * w.d_I * 2 + w.H_I * w.d_I * 2 + w.H_I * 4 + write)
 
 
 def source_hash():
@@ -565,6 +568,8 @@ def main(argv=None):
                     help="only time the write with the projected indexer key (profiling)")
     ap.add_argument("--mhc-only", action="store_true",
                     help="only time the single-pass mHC step (profiling)")
+    ap.add_argument("--decode-only", default=None, choices=sorted(ci.WORKLOADS), metavar="WORKLOAD",
+                    help="only time this decode workload, any schedule (profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--no-secondary", dest="secondary", action="store_false",
@@ -596,6 +601,15 @@ def main(argv=None):
         return 0
     if args.mhc_only:
         print(json.dumps(run_mhc(K, dev)), flush=True)
+        return 0
+    if args.decode_only:
+        w = ci.WORKLOADS[args.decode_only]
+        big = w.B * w.N >= (1 << 24)
+        r = run_workload(K, w, args.steps, args.warmup, dev, n_sets=1 if big else 2)
+        print(json.dumps({"workload": w.name, "schedule": w.schedule, "batch": w.B, "context": w.N,
+                          "ms_per_step": round(r["ms_per_step"], 4),
+                          "value": round(w.B / (r["ms_per_step"] * 1e-3), 1), "unit": "queries/s",
+                          "scan": {"kernel": r["scan_name"], "us": round(r["scan_ms"] * 1e3, 2)}}), flush=True)
         return 0
     w = ci.WORKLOADS[args.workload]
     if "F" not in w.schedule:
@@ -630,7 +644,7 @@ def main(argv=None):
                    "indexer": f"{w.H_I}x{w.d_I} bf16", "pool_blocks": w.P_b},
         "algorithmic_GBps": round(alg_q * w.B / (ms * 1e-3) / 1e9, 1),
         "roofline": {
-            "kernel": "score_kernel (Full-mode indexer scan with fused block max)",
+            "kernel": "score_kernel (Full-mode indexer scan with fused block max and the token's cache write)",
             "bound": "hbm",
             "achieved": round(scan_gbs, 1),
             "peak": HBM_PEAK_GBS,

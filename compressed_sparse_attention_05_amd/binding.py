@@ -72,6 +72,8 @@ SIGNATURES = {
     "csa2_mhc_step": (ctypes.c_int, [ctypes.POINTER(MhcArgs), P]),
     "csa2_index_score_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScoreArgs)]),
     "csa2_index_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, ctypes.c_size_t, P]),
+    "csa2_write_and_score": (ctypes.c_int, [P, ctypes.c_int, i32, P, P, P, P, ctypes.POINTER(ScoreArgs), P,
+                                            ctypes.c_size_t, P]),
     "csa2_topk_workspace_size": (ctypes.c_size_t, [i64, i64, i32]),
     "csa2_topk": (ctypes.c_int, [P, i64, i64, i64, i32, P, i32, P, P, ctypes.c_size_t, P]),
     "csa2_build_candidate_pool_workspace_size": (ctypes.c_size_t, [i64, i64, i32]),
@@ -287,6 +289,50 @@ def csa2_index_score(q_idx, w, k_idx, ctx_len, *, q_pos=None, m: int = 1, pool_b
     ws = _workspace(L.csa2_index_score_workspace_size(ctypes.byref(a)), q_idx.device)
     _check(L.csa2_index_score(ctypes.byref(a), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(stream)))
+    return scores, block_max
+
+
+def csa2_write_and_score(x, dst_row, codes, scales, idx_k_rows, q_idx, w, k_idx, ctx_len, *,
+                         pool_blocks=None, scores=None, ld: Optional[int] = None,
+                         want_block_max: bool = False, block_max=None, stream=None):
+    """A decode token's cache write (as mxfp4_kv_write of x [B][D] and
+    idx_k_rows [B][d_I] to flat rows dst_row [B] int64) and the scan that
+    follows it (as csa2_index_score with Tq == 1) in one launch.  dst_row[b]
+    must address a row of sequence b; other rows are not written.  Returns
+    (scores, block_max)."""
+    for t, nm in ((x, "x"), (dst_row, "dst_row"), (codes, "codes"), (scales, "scales"),
+                  (idx_k_rows, "idx_k_rows"), (q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx"),
+                  (ctx_len, "ctx_len")):
+        _dev(t, nm)
+    if dst_row.dtype != torch.int64 or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise TypeError("dst_row must be int64, codes/scales uint8")
+    B, Tq, H_I, d_I = q_idx.shape
+    cap = k_idx.shape[1]
+    D = x.shape[-1]
+    if Tq != 1 or x.shape[0] != B or tuple(idx_k_rows.shape) != (B, d_I) or dst_row.numel() != B:
+        raise ValueError("one new row, key and destination per sequence (Tq == 1)")
+    if idx_k_rows.dtype != k_idx.dtype:
+        raise ValueError("idx_k_rows must have the indexer cache's dtype")
+    if codes.numel() != B * cap * (D // 2) or scales.numel() != B * cap * (D // 16):
+        raise ValueError("codes/scales must hold B*cap rows of D channels")
+    P_b = 0
+    if pool_blocks is not None:
+        _dev(pool_blocks, "pool_blocks")
+        P_b = pool_blocks.shape[-1]
+    if ld is None:
+        ld = 8 * P_b if pool_blocks is not None else cap
+    if scores is None:
+        scores = torch.empty((B, 1, ld), dtype=torch.float32, device=q_idx.device)
+    if want_block_max and block_max is None:
+        block_max = torch.empty((B, 1, (ld + 7) // 8), dtype=torch.float32, device=q_idx.device)
+    a = ScoreArgs(q_idx=q_idx.data_ptr(), q_dtype=_dtype(q_idx, "q_idx"), w=w.data_ptr(),
+                  k_idx=k_idx.data_ptr(), k_dtype=_dtype(k_idx, "k_idx"), B=B, Tq=1, cap=cap,
+                  H_I=H_I, d_I=d_I, ctx_len=ctx_len.data_ptr(), q_pos=None, m=1,
+                  pool_blocks=None if pool_blocks is None else pool_blocks.data_ptr(), P_b=P_b,
+                  scores=scores.data_ptr(), ld_scores=ld,
+                  block_max=None if block_max is None else block_max.data_ptr())
+    _check(lib().csa2_write_and_score(_ptr(x), _dtype(x, "x"), D, _ptr(dst_row), _ptr(codes), _ptr(scales),
+                                      _ptr(idx_k_rows), ctypes.byref(a), None, 0, _stream(stream)))
     return scores, block_max
 
 

@@ -182,6 +182,39 @@ int csa2_index_score(const csa2_score_args* a, void* ws, size_t ws_bytes, void* 
 }
 
 // --------------------------------------------------------------------------
+int csa2_write_and_score(const void* x, int x_dtype, int32_t D, const int64_t* dst_row, uint8_t* codes,
+                         uint8_t* scales, const void* idx_k_rows, const csa2_score_args* a, void* ws,
+                         size_t ws_bytes, void* stream) {
+    int rc = check_score_args(a);
+    if (rc != CSA2_OK) return rc;
+    if (a->Tq != 1) return fail(CSA2_E_INVALID, "csa2_write_and_score: decode only (Tq must be 1)");
+    if (D <= 0 || D % 16 != 0)
+        return fail(CSA2_E_INVALID, "csa2_write_and_score: D=%d must be a positive multiple of 16", D);
+    if (!valid_dtype(x_dtype)) return fail(CSA2_E_INVALID, "csa2_write_and_score: bad x_dtype %d", x_dtype);
+    const int64_t nch = static_cast<int64_t>(a->d_I) * dtype_size(a->k_dtype) / 16;
+    if (D / 16 + nch > 256)
+        return fail(CSA2_E_UNSUPPORTED, "csa2_write_and_score: D/16 + indexer chunks = %lld exceeds one workgroup",
+                    static_cast<long long>(D / 16 + nch));
+    if (a->B == 0) return ok();
+    if (!x || !dst_row || !codes || !scales || !idx_k_rows)
+        return fail(CSA2_E_INVALID, "csa2_write_and_score: null pointer");
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(idx_k_rows, 16))
+        return fail(CSA2_E_INVALID, "csa2_write_and_score: x and idx_k_rows must be 16-byte and codes 8-byte aligned");
+    (void)ws; (void)ws_bytes;
+    csa2::ScoreLaunch p;
+    p.q_idx = a->q_idx; p.q_bf16 = a->q_dtype == CSA2_BF16;
+    p.w = a->w; p.k_idx = a->k_idx; p.k_bf16 = a->k_dtype == CSA2_BF16;
+    p.B = a->B; p.Tq = 1; p.cap = a->cap; p.H_I = a->H_I; p.d_I = a->d_I;
+    p.ctx_len = a->ctx_len; p.q_pos = a->q_pos; p.m = a->m;
+    p.pool = a->pool_blocks; p.P_b = a->pool_blocks ? a->P_b : 0;
+    p.scores = a->scores; p.ld = a->ld_scores;
+    p.block_max = a->block_max; p.ld_bm = (a->ld_scores + 7) / 8;
+    p.knew = idx_k_rows; p.wx = x; p.wx_bf16 = x_dtype == CSA2_BF16; p.wD = D; p.wdst = dst_row;
+    p.wcodes = codes; p.wscales = scales;
+    return device_status(csa2::launch_score(p, as_stream(stream)), "csa2_write_and_score");
+}
+
+// --------------------------------------------------------------------------
 size_t csa2_topk_workspace_size(int64_t rows, int64_t n, int32_t k) {
     (void)k;
     if (rows <= 0 || n <= 0) return 0;

@@ -33,6 +33,14 @@ struct ScoreLaunch {
     const int32_t* pool; int P_b;
     float* scores; int64_t ld;
     float* block_max; int64_t ld_bm;
+    // decode write in the same launch (knew == nullptr: none; Tq == 1):
+    // sequence b's MXFP4 row from wx[b] (wD channels) to flat row wdst[b]
+    // of wcodes/wscales and its indexer key knew[b] into k_idx, skipped
+    // unless wdst[b] lies in sequence b; its scores read the key from knew.
+    const void* knew = nullptr;
+    const void* wx = nullptr; bool wx_bf16 = false; int wD = 0;
+    const int64_t* wdst = nullptr;
+    uint8_t* wcodes = nullptr; uint8_t* wscales = nullptr;
 };
 bool score_shape_supported(int H_I, int d_I);
 hipError_t launch_score(const ScoreLaunch& p, hipStream_t st);

@@ -22,10 +22,14 @@
 //    order, so reads for the next channel overlap the current fmas.
 //  * The block max over 8 positions (candidate-pool input, notes section 3)
 //    is fused: 8 consecutive lanes own one block.
+#include <type_traits>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
 namespace {
+
+#include "mxfp4_quant.h"
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -42,9 +46,20 @@ struct ScoreArgs {
     int64_t units_per_row;    // ceil(n_slots / kUnit)
     int units_per_wg;
     int q_bf16;
+    // decode write in the same launch (knew == nullptr: none).  Workgroup
+    // column gx_scan of row b writes sequence b's new entry: its MXFP4 row
+    // from wx and its indexer key from knew (ROWB bytes per row), to flat
+    // row wdst[b], which must lie in sequence b (else nothing is written).
+    // Lanes scoring that position read the key from knew, so no workgroup
+    // of the launch reads what another one writes.
+    const uint8_t* knew;
+    const void* wx; int wx_bf16; int wD;
+    const int64_t* wdst;
+    uint8_t* wcodes; uint8_t* wscales;
+    int64_t gx_scan;
 };
 
-template <int HI, int DI, bool KBF16>
+template <int HI, int DI, bool KBF16, bool WR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(const void* __restrict__ q_all,
                                                          const float* __restrict__ w_all,
                                                          const uint8_t* __restrict__ k_all,
@@ -63,6 +78,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t row = blockIdx.y;       // query row (b * Tq + tq)
     const int64_t b = row / a.Tq;
+
+    if (WR && static_cast<int64_t>(blockIdx.x) == a.gx_scan) {
+        // the write column (decode: Tq == 1, row == b): threads [0, D/16)
+        // quantise one 16-channel block each, the next NCH threads copy one
+        // 16-byte chunk of the indexer key into the tiled cache
+        const int64_t dst = a.wdst[b];
+        if (dst < b * a.cap || dst >= (b + 1) * a.cap) return;
+        const int nblk = a.wD / 16;
+        if (t < nblk) {
+            float v[16];
+            if (a.wx_bf16) load_block<true>(a.wx, b, t, a.wD, v);
+            else load_block<false>(a.wx, b, t, a.wD, v);
+            quantise_block(v, t, a.wD, dst, a.wcodes, a.wscales);
+        } else if (t < nblk + NCH) {
+            const int c = t - nblk;
+            const uint4 val = *reinterpret_cast<const uint4*>(a.knew + b * ROWB + c * 16);
+            *reinterpret_cast<uint4*>(const_cast<uint8_t*>(k_all) + (((dst >> 6) * NCH + c) * 64 + (dst & 63)) * 16) = val;
+        }
+        return;
+    }
 
     // query -> LDS, transposed to [c][h], widened to float32
     for (int i = t; i < HI * DI; i += kThreads) {
@@ -103,15 +138,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     int64_t u1 = u0 + a.units_per_wg;
     if (u1 > a.units_per_row) u1 = a.units_per_row;
 
+    // position of the entry this launch writes for sequence b (-1: none);
+    // the unit holding it reads that row's key from knew (16-byte chunk
+    // stride) instead of the tiled cache (1 KiB chunk stride)
+    int64_t np = -1;
+    if (WR) {
+        const int64_t d = a.wdst[b] - b * a.cap;
+        np = (d >= 0 && d < a.cap) ? d : -1;
+    }
+    const uint8_t* knew_row = WR ? a.knew + b * ROWB : nullptr;
+
     for (int64_t u = u0 + wv; u < u1; u += kWaves) {
         int64_t slot[2], pos[2];
-        const uint8_t* base[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             slot[p] = u * kUnit + p * 64 + lane;
             pos[p] = pos_of(slot[p]);
+        }
+        const bool has_new = WR && np >= 0 && __ballot(pos[0] == np || pos[1] == np) != 0;   // wave-uniform
+        auto unit = [&](auto newrow) {
+        constexpr bool NR = decltype(newrow)::value;
+        const uint8_t* base[2];
+        int cstride[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
             const int64_t pp = pos[p] < 0 ? 0 : pos[p];
             base[p] = kb + ((pp >> 6) * NCH * 64 + (pp & 63)) * 16;
+            cstride[p] = 1024;
+            if (NR && pos[p] == np) { base[p] = knew_row; cstride[p] = 16; }
         }
         // Stream the row chunks in groups of G (registers hold the current
         // group and the next one in flight); the group loop is not unrolled
@@ -125,7 +179,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
-            for (int p = 0; p < 2; ++p) cur[p][j] = *reinterpret_cast<const uint4*>(base[p] + j * 1024);
+            for (int p = 0; p < 2; ++p) cur[p][j] = *reinterpret_cast<const uint4*>(base[p] + j * (NR ? cstride[p] : 1024));
         float acc[2][HI];
 #pragma unroll
         for (int p = 0; p < 2; ++p)
@@ -139,7 +193,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int j = 0; j < G; ++j)
 #pragma unroll
                 for (int p = 0; p < 2; ++p)
-                    nxt[p][j] = *reinterpret_cast<const uint4*>(base[p] + (gn * G + j) * 1024);
+                    nxt[p][j] = *reinterpret_cast<const uint4*>(base[p] + (gn * G + j) * (NR ? cstride[p] : 1024));
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const int c = g * G + j;
@@ -201,6 +255,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 if ((lane & 7) == 0 && blk < a.ld_bm) block_max[row * a.ld_bm + blk] = mx;
             }
         }
+        };
+        if (has_new) unit(std::true_type{});
+        else unit(std::false_type{});
     }
 }
 
@@ -222,10 +279,21 @@ hipError_t launch_typed(const ScoreLaunch& p, hipStream_t st) {
     const int64_t upw = kWaves;
     a.units_per_wg = static_cast<int>(upw);
     const int64_t gx = (a.units_per_row + upw - 1) / upw;
-    if (gx == 0 || rows == 0) return hipGetLastError();
-    score_kernel<HI, DI, KBF16><<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(rows)),
-                                  kThreads, 0, st>>>(p.q_idx, p.w, static_cast<const uint8_t*>(p.k_idx),
-                                                      p.scores, p.block_max, a);
+    a.knew = static_cast<const uint8_t*>(p.knew);
+    a.wx = p.wx; a.wx_bf16 = p.wx_bf16; a.wD = p.wD; a.wdst = p.wdst;
+    a.wcodes = p.wcodes; a.wscales = p.wscales;
+    a.gx_scan = gx;
+    const int64_t gx_all = gx + (p.knew ? 1 : 0);   // one more column writes the new entries
+    if (gx_all == 0 || rows == 0) return hipGetLastError();
+    // the write's code paths are a separate instantiation, so a scan without
+    // a write keeps its own register allocation
+    const dim3 grid(static_cast<unsigned>(gx_all), static_cast<unsigned>(rows));
+    if (p.knew)
+        score_kernel<HI, DI, KBF16, true><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, static_cast<const uint8_t*>(p.k_idx),
+                                                                     p.scores, p.block_max, a);
+    else
+        score_kernel<HI, DI, KBF16, false><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, static_cast<const uint8_t*>(p.k_idx),
+                                                                      p.scores, p.block_max, a);
     return hipGetLastError();
 }
 

@@ -77,7 +77,7 @@ class DecodeStep:
                  build_pool: bool = True, mfma_select: bool = False,
                  enc_caches: Optional[List[DecodeCache]] = None, enc_q_pos: Optional[torch.Tensor] = None,
                  enc_m: int = 2, enc_writes: Optional[List[Optional[tuple]]] = None,
-                 w_ik: Optional[torch.Tensor] = None):
+                 w_ik: Optional[torch.Tensor] = None, fuse_write: bool = True):
         """w_ik: [D][d_I] float32 indexer-K projection weights; when given, the
         token's indexer key is projected from new_kv in the same launch as its
         MXFP4 write (csa2_kv_write_project) instead of passed as new_kidx.
@@ -85,7 +85,11 @@ class DecodeStep:
         enc_q_pos: [B] int64 absolute position of the token in each sequence
         (E layers' visibility).  enc_writes: per E layer, None or
         (new_kv [B][D], new_kidx [B][d_I], dst_row [B] int64) for an entry
-        the token completes, written before any scoring."""
+        the token completes, written before any scoring.
+        fuse_write: when the step's first call after the write is the scan
+        of the main cache, do both in one launch (csa2_write_and_score); then
+        dst_row[b] must address a row of sequence b (other rows are not
+        written), as a decode token's entry always does."""
         assert len(schedule) == len(layers)
         n_enc = schedule.count("E")
         enc_caches = list(enc_caches or [])
@@ -103,6 +107,7 @@ class DecodeStep:
         self.B, self.cap, self.D = B, cap, D
         self.L = bd.lib()
         self.calls = []          # (name, fn, args) in launch order
+        self._fusable_write = None
         self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(D)
         self._keep = []          # keep ctypes structs and tensors alive
 
@@ -125,6 +130,13 @@ class DecodeStep:
                     n_cache_rows, bd._ptr(cache.codes), bd._ptr(cache.scales), bd._ptr(new_kidx), kdt,
                     d_I if new_kidx is not None else 0, bd._ptr(cache.k_idx), None)
             self.calls.append(("write", self.L.mxfp4_kv_write, args))
+            nch = d_I * new_kidx.element_size() // 16 if new_kidx is not None else 0
+            if (fuse_write and new_kidx is not None and new_kv.shape[0] == B and D // 16 + nch <= 256
+                    and new_kidx.dtype == cache.k_idx.dtype and tuple(new_kidx.shape) == (B, d_I)):
+                # (x, x_dtype, D, dst_row, codes, scales, idx_k_rows): the
+                # write half of csa2_write_and_score
+                self._fusable_write = (bd._ptr(new_kv), bd._dtype(new_kv, "new_kv"), D, bd._ptr(dst_row),
+                                       bd._ptr(cache.codes), bd._ptr(cache.scales), bd._ptr(new_kidx))
         for ei, wr in enumerate(enc_writes or []):
             if wr is None:
                 continue
@@ -192,8 +204,13 @@ class DecodeStep:
                 nws = self.L.csa2_index_score_workspace_size(ctypes.byref(sa))
                 ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
                 self._keep += [sa, ws]
-                self.calls.append((f"score{li}", self.L.csa2_index_score,
-                                   (ctypes.byref(sa), bd._ptr(ws), nws, None)))
+                if self._fusable_write is not None and len(self.calls) == 1 and self.calls[0][0] == "write":
+                    # nothing runs between the write and this scan: one launch
+                    self.calls[0] = (f"score{li}", self.L.csa2_write_and_score,
+                                     self._fusable_write + (ctypes.byref(sa), bd._ptr(ws), nws, None))
+                else:
+                    self.calls.append((f"score{li}", self.L.csa2_index_score,
+                                       (ctypes.byref(sa), bd._ptr(ws), nws, None)))
                 fused = False
                 # The Full top-k may be taken inside a pool only when that pool
                 # was selected from this same layer's block maxima (the top-k

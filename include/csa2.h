@@ -164,6 +164,34 @@ size_t csa2_index_score_workspace_size(const csa2_score_args *a);
 int csa2_index_score(const csa2_score_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * csa2_write_and_score - a decode token's cache write ([KVC] section 4, as
+ * mxfp4_kv_write) and the first scan of its step (as csa2_index_score, Full
+ * or Reindex mode) in one launch.  The results are those of
+ *     mxfp4_kv_write(x, x_dtype, a->B, D, dst_row, a->B * a->cap, codes,
+ *                    scales, idx_k_rows, a->k_dtype, a->d_I, a->k_idx)
+ *     csa2_index_score(a)
+ * in that order, with one rule on the rows: sequence b's entry is written
+ * only when dst_row[b] lies in sequence b (b*cap <= dst_row[b] < (b+1)*cap);
+ * any other row is skipped (nothing written, nothing scored differently).
+ * The scan reads each new entry's indexer key from idx_k_rows, so no part
+ * of the launch reads a row another part writes.
+ *
+ * x          [B][D] new main-KV rows (CSA2_F32 or CSA2_BF16), 16-byte aligned
+ * dst_row    [B] int64 flat destination rows (see above)
+ * codes, scales  the MXFP4 cache (as mxfp4_kv_write), codes 8-byte aligned
+ * idx_k_rows [B][d_I] new indexer keys in a->k_dtype, 16-byte aligned
+ * a          as csa2_index_score, with Tq == 1; a->k_idx is the tiled
+ *            indexer cache that receives the keys
+ * Errors: those of csa2_index_score; Tq != 1, bad D (D % 16 != 0) or
+ * x_dtype, null or misaligned pointers give CSA2_E_INVALID; D/16 plus the
+ * indexer row's 16-byte chunks above 256 gives CSA2_E_UNSUPPORTED.  No
+ * workspace is needed (ws may be NULL).  Caller owns every buffer.
+ * ------------------------------------------------------------------------ */
+int csa2_write_and_score(const void *x, int x_dtype, int32_t D, const int64_t *dst_row, uint8_t *codes,
+                         uint8_t *scales, const void *idx_k_rows, const csa2_score_args *a, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * csa2_topk - exact top-k per row ([KVC] sections 2-3): order by score
  * descending, then slot ascending (-0 equals +0); -inf slots are never
  * chosen.  Writes min(k, #finite) entries in ascending order, then -1.

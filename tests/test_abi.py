@@ -205,3 +205,26 @@ def test_noalloc_attention_rejects_calls_beyond_its_scratch_on_host():
     assert L.csa2_sparse_attn_decode_noalloc(None, None) == 1
     a.H, a.B = 64, 0
     assert L.csa2_sparse_attn_decode_noalloc(ctypes.byref(a), None) == 0    # nothing to do
+
+
+def test_write_and_score_argument_checks():
+    L = binding.lib()
+    P = 1 << 12                 # stands in for a device address: only host checks run
+    a = binding.ScoreArgs(q_idx=P, q_dtype=1, w=P, k_idx=P, k_dtype=1, B=2, Tq=1, cap=128,
+                     H_I=8, d_I=128, ctx_len=P, q_pos=None, m=1, pool_blocks=None, P_b=0, scores=P,
+                     ld_scores=128, block_max=None)
+    call = lambda D=512, x=P, dst=P, kr=P, dt=1: L.csa2_write_and_score(
+        x, dt, D, dst, P, P, kr, ctypes.byref(a), None, 0, None)
+    assert call(D=8) == 1 and "multiple of 16" in _err()
+    assert call(dt=7) == 1
+    assert call(x=None) == 1 and "null" in _err()
+    assert call(kr=None) == 1
+    assert call(kr=P + 8) == 1 and "aligned" in _err()
+    # one workgroup writes a row: D/16 blocks plus 16 indexer chunks must fit 256 threads
+    assert call(D=4096) == 2
+    a.Tq = 2
+    assert call() == 1 and "Tq" in _err()
+    a.Tq, a.cap = 1, 100
+    assert call() == 1       # the scan's own checks (tiled cache needs cap % 64 == 0)
+    a.cap, a.B = 128, 0
+    assert call() == 0

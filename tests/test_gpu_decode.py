@@ -25,13 +25,16 @@ def K():
     return K
 
 
-@pytest.mark.parametrize("k,P_b,mfma,project", [(256, 512, False, False), (600, 512, False, False),
-                                                (256, 512, True, False), (256, 512, False, True)])
-def test_decode_step_full_reindex_reuse(K, k, P_b, mfma, project):
+@pytest.mark.parametrize("k,P_b,mfma,project,fuse", [(256, 512, False, False, True), (600, 512, False, False, True),
+                                                     (256, 512, True, False, True), (256, 512, False, True, True),
+                                                     (256, 512, False, False, False)])
+def test_decode_step_full_reindex_reuse(K, k, P_b, mfma, project, fuse):
     # k <= P_b: the Full layer's pool and top-k run as one launch (or, with
     # mfma, the matrix-core scan and the band-exact selection);
     # k > P_b: pool, then the Full top-k over the whole row.  With project,
     # the token's indexer key is projected from its latent row by the write.
+    # fuse: the write shares the Full scan's launch (csa2_write_and_score)
+    # when the step allows it; off, it is a launch of its own.
     from compressed_sparse_attention_05_amd.decode import DecodeCache, DecodeStep, LayerInputs
     dev = torch.device("cuda:0")
     B, cap, D, H, d_I, H_I, W = 2, 20032, 512, 64, 128, 8, 128
@@ -72,7 +75,9 @@ def test_decode_step_full_reindex_reuse(K, k, P_b, mfma, project):
                       new_kv=flat_kv[new_rows.to(dev)].contiguous(),
                       new_kidx=None if project else kidx.reshape(B * cap, d_I)[new_rows].contiguous().to(dev),
                       dst_row=new_rows.to(dev), mfma_select=mfma,
-                      w_ik=w_ik.to(dev) if project else None)
+                      w_ik=w_ik.to(dev) if project else None, fuse_write=fuse)
+    names = [c[1].__name__ for c in step.calls]
+    assert ("csa2_write_and_score" in names) == (fuse and not mfma and not project), names
     step.run()
     torch.cuda.synchronize()
     sm = 1.0 / math.sqrt(D)
