@@ -21,6 +21,15 @@ hipError_t launch_kv_write_project(const void* x, bool x_bf16, int64_t n_rows, i
                                    int64_t n_cache_rows, uint8_t* codes, uint8_t* scales, const float* W,
                                    int d_I, void* kcache, hipStream_t st);
 
+// Monotone 32-bit key of a score for the selections: strictly increasing
+// in the score with -0 == +0; 0 is reserved for -inf (an empty slot).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0xff800000u) return 0u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 struct ScoreLaunch {
     const void* q_idx; bool q_bf16;
     const float* w;

@@ -66,12 +66,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 }
 
 
-__device__ __forceinline__ uint32_t key_of(float v) {
-    uint32_t u = __float_as_uint(v);
-    if (u == 0xff800000u) return 0u;      // -inf: empty
-    if (u == 0x80000000u) u = 0u;         // -0 -> +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+__device__ __forceinline__ uint32_t key_of(float v) { return order_key(v); }
 
 // Exclusive prefix of `flag` over the workgroup in thread order, plus the total.
 __device__ __forceinline__ uint32_t block_excl_prefix(bool flag, uint32_t* wave_tot, uint32_t& total) {
@@ -341,14 +336,16 @@ __device__ __forceinline__ uint32_t sel_stats(const uint32_t (&kk)[R], SelLds& s
 // is exactly the selection.  Random scores reach that after two passes
 // instead of running down to bit 0.  Without EARLY the result is the exact
 // need-th key.
+// sel_passes_from: the same passes when the keys that can hold the result
+// are known to share the bits above `top` with value `known` (keys with other
+// high bits are counted as above when larger, which the caller has already
+// subtracted from need, or are never chosen when smaller).  hist[0] must be
+// clear.
 template <int R, bool EARLY = false>
-__device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t mn, uint32_t mx, uint32_t& need,
-                                               SelLds& sh) {
-    if (mn == mx) return mn;                       // every nonempty key is T
+__device__ __forceinline__ uint32_t sel_passes_from(const uint32_t (&kk)[R], int top, uint64_t known, uint32_t& need,
+                                                    SelLds& sh) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int hb = kSelBins - 8 - 8 * tid;         // this thread's bins
-    int top = 31 - __builtin_clz(mn ^ mx);         // highest bit not shared
-    uint64_t known = static_cast<uint64_t>(mn) >> (top + 1);
     int buf = 0;
     while (top >= 0) {
         const int nb = top + 1 < kSelBits ? top + 1 : kSelBits;
@@ -434,24 +431,22 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
     return static_cast<uint32_t>(known);
 }
 
-// Choose the k best keys of the workgroup's slots (thread t: slots
-// [tR, tR + R) in kk, 0 = empty) and call out(rank, j) for each chosen slot
-// tR + j in ascending slot order.  Returns min(k, #nonempty).
-// If lb is given, *lb is set to a key no larger than any chosen key (every
-// chosen key is >= *lb; 0 when nothing is chosen).
-template <int R, class Out>
-__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out, uint32_t* lb = nullptr) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    uint32_t mn, mx;
-    const uint32_t n_valid = sel_stats<R>(kk, sh, mn, mx);
-    const uint32_t k_eff = n_valid < k ? n_valid : k;
-    if (lb) *lb = 0u;
-    if (k_eff == 0) return 0;
-    uint32_t need = k_eff;
-    const uint32_t T = sel_passes<R, true>(kk, mn, mx, need, sh);
-    if (lb) *lb = need == 0 ? T + 1u : T;
+template <int R, bool EARLY = false>
+__device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t mn, uint32_t mx, uint32_t& need,
+                                               SelLds& sh) {
+    if (mn == mx) return mn;                       // every nonempty key is T
+    const int top = 31 - __builtin_clz(mn ^ mx);   // highest bit not shared
+    return sel_passes_from<R, EARLY>(kk, top, static_cast<uint64_t>(mn) >> (top + 1), need, sh);
+}
 
-    // ---- 3. ordered emission: one scan of (above << 16 | ties)
+// Stage 3, ordered emission of the keys above T plus the first `need` keys
+// equal to T: one scan of (above << 16 | ties) gives each thread its output
+// offset and its share of the ties; out(rank, j) for each chosen slot in
+// ascending slot order.  Ends with a barrier.
+template <int R, class Out>
+__device__ __forceinline__ void sel_emit(const uint32_t (&kk)[R], uint32_t T, uint32_t need, uint32_t k, SelLds& sh,
+                                         Out out) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     uint32_t above = 0, ties = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j) { above += kk[j] > T; ties += kk[j] == T; }
@@ -478,6 +473,27 @@ __device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, 
         if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
+}
+
+// Choose the k best keys of the workgroup's slots (thread t: slots
+// [tR, tR + R) in kk, 0 = empty) and call out(rank, j) for each chosen slot
+// tR + j in ascending slot order.  Returns min(k, #nonempty).
+// If lb is given, *lb is set to a key no larger than any chosen key (every
+// chosen key is >= *lb; 0 when nothing is chosen); max_key receives the
+// largest key.
+template <int R, class Out>
+__device__ uint32_t select_run(const uint32_t (&kk)[R], uint32_t k, SelLds& sh, Out out, uint32_t* lb = nullptr,
+                               uint32_t* max_key = nullptr) {
+    uint32_t mn, mx;
+    const uint32_t n_valid = sel_stats<R>(kk, sh, mn, mx);
+    if (max_key) *max_key = mx;
+    const uint32_t k_eff = n_valid < k ? n_valid : k;
+    if (lb) *lb = 0u;
+    if (k_eff == 0) return 0;
+    uint32_t need = k_eff;
+    const uint32_t T = sel_passes<R, true>(kk, mn, mx, need, sh);
+    if (lb) *lb = need == 0 ? T + 1u : T;
+    sel_emit<R>(kk, T, need, k, sh, out);
     return k_eff;
 }
 

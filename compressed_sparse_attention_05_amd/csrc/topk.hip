@@ -382,22 +382,28 @@ __global__ __launch_bounds__(kThreads) void pool_topk_kernel(const float* __rest
     __shared__ SelLds sh;
     __shared__ int32_t pool_s[kPoolMax];
     const int64_t row = blockIdx.x;
-    uint32_t got_pool = 0, pool_lb = 0;
+    uint32_t got_pool = 0, pool_lb = 0, max_key = 0xffffffffu;
     {
         const float* bm = bmax + row * ld_bm;
         int32_t* po = pool + row * static_cast<int64_t>(P_b);
         const int64_t r0 = static_cast<int64_t>(threadIdx.x) * R1;
         uint32_t kk[R1];
         load_run_keys<R1>(bm, r0, n_blocks, kk);
-        got_pool = select_run<R1>(kk, static_cast<uint32_t>(P_b), sh, [&](uint32_t r, int j) {
+        auto emit = [&](uint32_t r, int j) {
             po[r] = static_cast<int32_t>(r0) + j;
             pool_s[r] = static_cast<int32_t>(r0) + j;
-        }, &pool_lb);
+        };
+        got_pool = select_run<R1>(kk, static_cast<uint32_t>(P_b), sh, emit, &pool_lb, &max_key);
         const uint32_t got = got_pool;
         for (int i = static_cast<int>(got) + threadIdx.x; i < P_b; i += kThreads) {
             po[i] = -1;
             pool_s[i] = -1;
         }
+        // hist[0] for the top-k passes (every read of it ended before the
+        // emission's last barrier)
+        const int hb = kSelBins - 8 - 8 * threadIdx.x;
+        *reinterpret_cast<uint4*>(&sh.hist[0][hb]) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sh.hist[0][hb + 4]) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
     const float* s = scores + row * ld;
@@ -429,13 +435,21 @@ __global__ __launch_bounds__(kThreads) void pool_topk_kernel(const float* __rest
     // >= k blocks at least k pool scores are >= pool_lb and the k-th best
     // score is too: scores below it cannot be chosen and leave the
     // selection as empty slots, which keeps them out of its histograms.
+    // With a full pool those scores also lie in [pool_lb, max_key] (no score
+    // exceeds the largest block maximum) and at least k of them are
+    // nonempty, so the selection needs no count or range pass of its own.
+    auto out_pos = [&](uint32_t r, int j) { o[r] = blk[j >> 3] * 8 + (j & 7); };
+    uint32_t got;
     if (got_pool == static_cast<uint32_t>(P_b) && pool_lb != 0u) {
 #pragma unroll
         for (int e = 0; e < R2; ++e) kk[e] = kk[e] >= pool_lb ? kk[e] : 0u;
+        uint32_t need = static_cast<uint32_t>(k);
+        const uint32_t T = sel_passes<R2, true>(kk, pool_lb, max_key, need, sh);
+        sel_emit<R2>(kk, T, need, static_cast<uint32_t>(k), sh, out_pos);
+        got = static_cast<uint32_t>(k);
+    } else {
+        got = select_run<R2>(kk, static_cast<uint32_t>(k), sh, out_pos);
     }
-    const uint32_t got = select_run<R2>(kk, static_cast<uint32_t>(k), sh, [&](uint32_t r, int j) {
-        o[r] = blk[j >> 3] * 8 + (j & 7);
-    });
     for (int i = static_cast<int>(got) + threadIdx.x; i < k; i += kThreads) o[i] = -1;
 }
 
@@ -449,15 +463,12 @@ hipError_t launch_pool_topk(const float* bmax, int64_t rows, int64_t n_blocks, i
                             int32_t* pool, const float* scores, int64_t ld, int k, int32_t* out, hipStream_t st) {
     if (rows == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(rows));
-    const bool r1_16 = n_blocks <= 16 * kThreads, r2_16 = 8 * P_b <= 16 * kThreads;
-    if (r1_16 && r2_16)
+    // the pool's 8*P_b <= 16,384 scores always fit 16 per thread (P_b <= 2,048)
+    static_assert(8 * kPoolMax <= 16 * kThreads, "pool scores: 16 per thread");
+    if (n_blocks <= 16 * kThreads)
         pool_topk_kernel<16, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
-    else if (r1_16)
-        pool_topk_kernel<16, 32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
-    else if (r2_16)
-        pool_topk_kernel<32, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
     else
-        pool_topk_kernel<32, 32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+        pool_topk_kernel<32, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
     return hipGetLastError();
 }
 
