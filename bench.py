@@ -44,6 +44,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16/fp16 matrix peak, vendor figure
 METRIC = "CSA2 decode queries/s & achieved HBM GB/s at 128K and 1M ctx (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_scan_traffic.json")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 
 # --------------------------------------------------------------------------
@@ -180,12 +181,28 @@ def scan_bytes_per_launch(w: ci.Workload):
     return w.B * (w.N * w.d_I * 2 + w.H_I * w.d_I * 2 + w.H_I * 4 + write)
 
 
-def source_hash():
+def source_hash(f="score.hip"):
     h = hashlib.sha256()
-    for f in ("score.hip",):
-        with open(os.path.join(ROOT, "compressed_sparse_attention_05_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    with open(os.path.join(ROOT, "compressed_sparse_attention_05_amd", "csrc", f), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def attn_traffic_for(workload_name):
+    """Counter-measured bytes per launch of the attention and combine kernels
+    (profiles/attn_traffic.json), while attn.hip is the source they were
+    taken on; None otherwise."""
+    try:
+        with open(ATTN_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash("attn.hip"):
+        return None
+    out = {k["kernel"]: {"read_bytes": k["read_bytes"], "written_bytes": k["written_bytes"],
+                         "algorithmic_read_bytes": k["algorithmic_read_bytes"]}
+           for k in rec.get("kernels", []) if k.get("workload") == workload_name}
+    return out or None
 
 
 def traffic_for(workload_name):
@@ -654,6 +671,9 @@ def main(argv=None):
             "scan_us": round(r["scan_ms"] * 1e3, 2),
             "bytes_per_launch": scan_bytes,
         },
+        # HBM bytes per launch of the attention kernels from FETCH_SIZE /
+        # WRITE_SIZE (calibrated), null once their source has changed
+        "attention_traffic": attn_traffic_for(w.name),
     }
     if args.cpu_queries > 0:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
