@@ -31,6 +31,8 @@
 // most 5 significant bits, range 2^-10..2688) and bf16 q / SWA values in
 // [2^-14, 65504] are fp16 numbers, so the operands are exact; MFMA sums in
 // float32; only P is rounded (to fp16, relative 2^-11).
+#include <type_traits>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -86,6 +88,26 @@ __device__ __forceinline__ void dequant8_hw(uint32_t cw, uint32_t sc, uint32_t o
     out[1] = __builtin_bit_cast(uint32_t, v1 * s);
     out[2] = __builtin_bit_cast(uint32_t, v2 * s);
     out[3] = __builtin_bit_cast(uint32_t, v3 * s);
+}
+
+// 32 channels (a 16-byte code run) under their two scale bytes (sc: the
+// bytes of channels 0..15 and 16..31): dequant8_hw four times, with each
+// scale converted once.  out[4e + j]: channels 8e + 2j, 8e + 2j + 1.
+__device__ __forceinline__ void dequant32_hw(const uint4& cw4, uint32_t sc, uint32_t (&out)[16]) {
+    uint32_t c0 = sc & 0x7fu, c1 = (sc >> 8) & 0x7fu;
+    c0 = c0 < 0x7eu ? c0 : 0x7eu;
+    c1 = c1 < 0x7eu ? c1 : 0x7eu;
+    const half2v s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0 | (c0 << 8), 1.0f, false);
+    const half2v s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1 | (c1 << 8), 1.0f, false);
+    const uint32_t cw[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const half2v s = e < 2 ? s0 : s1;
+        out[4 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 0) * s);
+        out[4 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 1) * s);
+        out[4 * e + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 2) * s);
+        out[4 * e + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 3) * s);
+    }
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -514,36 +536,38 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
 //     online softmax of that block and its P fragments;
 //   D-waves 4..7 (channel slice dw = w - 4): O^T[128 d][64 heads] += V^T P^T
 //     with V^T read transposed from Kt.
-// Every wave gathers and dequantises 8 keys (8w .. 8w + 7) of the next tile
-// into the other Kt buffer.  Per tile two phases separated by barriers:
-//   phase 1: S-waves S(i) and their block max   || D-waves P.V(i - 1)
-//   phase 2: S-waves softmax(i) -> P, rescale; then all waves dequant(i + 1)
-//            and issue the gathers of tile i + 2
-// so the matrix cores of every SIMD get work from both roles and no S
-// partial sums cross waves (each S-wave covers all channels).  The gathers
-// are buffer loads whose row offset is a plain integer (rows beyond the
-// cache read zeros); one load path per instantiation, since a branch between
-// buffer and global loads makes the compiler wait for every gather where the
-// paths join.
-// Start-up: the first tile's gathers go out first (index entries straight
-// from global memory), then the unit's q is read once by all 512 threads in
-// 1 KiB runs and staged in the second Kt buffer, from which each S-wave
-// takes its fragments.  A split's generic tiles (window rows, or a tile
-// straddling the main/window boundary) come first, the first of them loaded
-// during start-up; the online softmax does not depend on the order beyond
-// rounding.
+// A D-wave also gathers and dequantises its own 128 channels of every tile:
+// those are the only channels it reads in P.V, so it can overwrite the tile
+// it has just consumed with the next one as soon as its own P.V of it is
+// done, without waiting for any other wave.  One barrier per tile:
+//   S-waves: S(i) on Kt[i & 1] and the block max; the tile max with the
+//            partner key block (a two-wave handshake in LDS); softmax -> P(i)
+//   D-waves: O += V(i - 1) P(i - 1) from Kt[(i - 1) & 1]; then tile i + 1
+//            into that buffer; then the gathers of tile i + 2 into registers
+// P, the rescale factors and their flags alternate between two LDS copies.
+// Each role runs its own copy of the tile loop (the same barriers), so the
+// two roles' registers are allocated separately.  No S partial sums cross
+// waves (each S-wave covers all channels).  The gathers are buffer loads
+// whose row offset is a plain integer (rows beyond the cache read zeros);
+// one load path per instantiation, since a branch between buffer and global
+// loads makes the compiler wait for every gather where the paths join.
+// Start-up: the first main tile's gathers go out first (index entries
+// straight from global memory), then the unit's q is read once by all 512
+// threads in 1 KiB runs and staged in the second Kt buffer, from which each
+// S-wave takes its fragments.  A split's generic tiles (window rows, or a
+// tile that mixes main and window rows) come first and are loaded directly.
 template <bool BF16, bool USE_BUF>
 __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     constexpr int D = 512, KT = 64, KROW = D + 8, SSTEPS = D / 16;
     __shared__ __attribute__((aligned(16))) _Float16 Kt[2][KT * KROW];
-    __shared__ __attribute__((aligned(16))) uint4 Pb[2][4][64];   // [head group][k-step][lane]
+    __shared__ __attribute__((aligned(16))) uint4 Pb[2][2][4][64];   // [parity][head group][k-step][lane]
     __shared__ __attribute__((aligned(16))) float kmask[2][KT];
-    __shared__ float Lm[2][2][32];                                 // block max [hg][kb][head]
-    __shared__ float alpha_s[64];
-    __shared__ int grow_s[2];
+    __shared__ float Lm[2][2][32];                                 // tile max [hg][kb][head]
+    __shared__ float alpha_s[2][64];
+    __shared__ int grow_s[2][2];
+    __shared__ int pair_it[2][2];                                  // [hg][kb]: iteration whose Lm is posted
     __shared__ float Lsum[2][2][32];
     __shared__ float Mfin[64];
-    __shared__ int32_t idx_s[KT * kMaxTilesPerSplit];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -586,128 +610,137 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     auto tile_of = [&](int it) { return it < n_gen ? t_first_gen + it : t_begin + (it - n_gen); };
     auto is_main = [&](int it) { return it >= n_gen; };
 
-    // ---- gathers: lane l takes key 4g + l / 16 of this wave's group g and
-    // its channels 32(l % 16) .. + 31 (16 code bytes, 2 scale bytes), so a
-    // group is one 16-byte load and one 2-byte load per lane
-    constexpr int KPW = KT / 8;                       // keys gathered per wave
-    uint4 pm_c[2];
-    uint32_t pm_s[2];
+    // ---- D-wave slices: lane l takes key l / 4 + 16 g (g = 0..3) of a tile
+    // and channels 128 dw + 32 (l % 4) .. + 31 of it: one 16-byte code load
+    // and one 2-byte scale load per key
+    const int sp = lane & 3, skey = lane >> 2;
+    uint4 pm_c[4];
+    uint32_t pm_s[4];
     uint32_t pm_ok = 0;                               // bit g: this lane's key of group g is a real row
+    int32_t nidx[4];                                  // index entries of the next main tile to gather
     const __amdgpu_buffer_rsrc_t rc_codes = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.codes + kvbase * (D / 2)), static_cast<short>(0),
         USE_BUF ? static_cast<int>(a.cap * (D / 2)) : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rc_scales = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.scales + kvbase * (D / 16)), static_cast<short>(0),
         USE_BUF ? static_cast<int>(a.cap * (D / 16)) : 0, 0x00020000);
-    const int gpart = lane & 15, gkey = lane >> 4;
-    auto gather_rows = [&](const int32_t (&row)[2]) {
+    int nidx_tile = -1;                               // the tile nidx holds (wave-uniform)
+    auto load_idx = [&](int tile) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) nidx[g] = idx[tile * KT + skey + 16 * g];
+        nidx_tile = tile;
+    };
+    auto gather_slice = [&]() {
         pm_ok = 0;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const bool ok = row[g] >= 0 && row[g] < a.cap;
-            const int32_t rw = ok ? row[g] : 0;
+        for (int g = 0; g < 4; ++g) {
+            const bool ok = nidx[g] >= 0 && nidx[g] < a.cap;
+            const int32_t rw = ok ? nidx[g] : 0;
             pm_ok |= ok ? (1u << g) : 0u;
             if constexpr (USE_BUF) {
                 pm_c[g] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        rc_codes, rw * (D / 2) + 16 * gpart, 0, 0));
-                pm_s[g] = __builtin_amdgcn_raw_buffer_load_b16(rc_scales, rw * (D / 16) + 2 * gpart, 0, 0);
+                                                        rc_codes, rw * (D / 2) + 64 * dw + 16 * sp, 0, 0));
+                pm_s[g] = __builtin_amdgcn_raw_buffer_load_b16(rc_scales, rw * (D / 16) + 8 * dw + 2 * sp, 0, 0);
             } else {
                 const int64_t rr = kvbase + rw;
-                pm_c[g] = *reinterpret_cast<const uint4*>(a.codes + rr * (D / 2) + 16 * gpart);
-                pm_s[g] = *reinterpret_cast<const uint16_t*>(a.scales + rr * (D / 16) + 2 * gpart);
+                pm_c[g] = *reinterpret_cast<const uint4*>(a.codes + rr * (D / 2) + 64 * dw + 16 * sp);
+                pm_s[g] = *reinterpret_cast<const uint16_t*>(a.scales + rr * (D / 16) + 8 * dw + 2 * sp);
             }
         }
     };
-    int win0 = t_begin;
-    auto stage_idx = [&](int first_tile) {
-        win0 = first_tile;
-        for (int i = tid; i < kMaxTilesPerSplit * KT; i += 512) {
-            const int slot = first_tile * KT + i;
-            idx_s[i] = slot < a.k ? idx[slot] : -1;
-        }
+    // gather main tile `it_` into registers, then fetch the next main
+    // tile's index entries so the following gather need not wait for them
+    auto gather_main = [&](int it_) {
+        if (nidx_tile != tile_of(it_)) load_idx(tile_of(it_));
+        gather_slice();
+        if (it_ + 1 < n_it && is_main(it_ + 1)) load_idx(tile_of(it_ + 1));
     };
-    // main tile `tile`: index entries from the staged window
-    auto prefetch_main = [&](int tile) {
-        int32_t row[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) row[g] = idx_s[tile * KT + KPW * wv + 4 * g + gkey - win0 * KT];
-        gather_rows(row);
-    };
-    // one key row (all lanes, 8 channels each); every lane writes the mask
-    // entry (the same value), so the write needs no branch
-    auto store_key = [&](int buf, int key, const uint32_t (&h)[4], bool valid) {
-        *reinterpret_cast<uint4*>(&Kt[buf][key * KROW + 8 * lane]) = make_uint4(h[0], h[1], h[2], h[3]);
-        kmask[buf][key] = valid ? 0.0f : -__builtin_inff();
-    };
-    auto dequant_prefetched = [&](int buf) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int key = KPW * wv + 4 * g + gkey;
+    // rows are KROW = 520 halves (1,040 bytes) apart, so the 16 keys of one
+    // store instruction start 4 banks apart and its 64 lanes spread evenly
+    // over the banks in the plain piece order
+    auto dequant_group = [&](int buf, int g) {
+        {
+            const int key = skey + 16 * g;
+            _Float16* dst = &Kt[buf][key * KROW + 128 * dw + 32 * sp];
+            const uint32_t sc = pm_s[g];
+            uint32_t c0 = sc & 0x7fu, c1 = (sc >> 8) & 0x7fu;
+            c0 = c0 < 0x7eu ? c0 : 0x7eu;
+            c1 = c1 < 0x7eu ? c1 : 0x7eu;
+            const half2v s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0 | (c0 << 8), 1.0f, false);
+            const half2v s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1 | (c1 << 8), 1.0f, false);
             const uint32_t cw[4] = {pm_c[g].x, pm_c[g].y, pm_c[g].z, pm_c[g].w};
-            _Float16* dst = &Kt[buf][key * KROW + 32 * gpart];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // rotate the 16-byte pieces by the lane so neighbouring lanes
-                // write different banks
-                const int ee = (e + gpart) & 3;
-                uint32_t h[4];
-                dequant8_hw(cw[ee], (pm_s[g] >> (8 * (ee >> 1))) & 0xffu, h);
-                *reinterpret_cast<uint4*>(dst + 8 * ee) = make_uint4(h[0], h[1], h[2], h[3]);
+                const half2v sv = e < 2 ? s0 : s1;
+                const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 0) * sv);
+                const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 1) * sv);
+                const uint32_t h2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 2) * sv);
+                const uint32_t h3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 3) * sv);
+                *reinterpret_cast<uint4*>(dst + 8 * e) = make_uint4(h0, h1, h2, h3);
             }
             // an empty slot keeps the finite values of the clamped row; its
             // logit is -inf, so it enters P.V with weight exactly 0
-            kmask[buf][key] = ((pm_ok >> g) & 1u) ? 0.0f : -__builtin_inff();
+            if (dw == 0 && sp == 0) kmask[buf][key] = ((pm_ok >> g) & 1u) ? 0.0f : -__builtin_inff();
         }
     };
-    // any tile (main rows, window rows, empty slots), loaded and stored at
-    // once; index entries straight from global memory
-    auto load_generic = [&](int tile, int buf) {
-        for (int i = 0; i < KPW; ++i) {
-            const int key = KPW * wv + i;
+    auto dequant_slice = [&](int buf) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dequant_group(buf, g);
+    };
+    // this D-wave's slice of any tile (main rows, window rows, empty
+    // slots), loaded and stored at once; index entries from global memory
+    auto load_generic_slice = [&](int tile, int buf) {
+#pragma unroll 1
+        for (int g = 0; g < 4; ++g) {
+            const int key = skey + 16 * g;
             const int slot = tile * KT + key;
-            uint32_t h[4] = {0u, 0u, 0u, 0u};
+            uint32_t h[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) h[i] = 0u;
             bool valid = false;
             if (slot < a.k) {
-                const int32_t row = __builtin_amdgcn_readfirstlane(idx[slot]);
+                const int32_t row = idx[slot];
                 valid = row >= 0 && row < a.cap;
                 const int64_t rr = kvbase + (valid ? row : 0);
-                const uint32_t cw = *reinterpret_cast<const uint32_t*>(a.codes + rr * (D / 2) + 4 * lane);
-                const uint32_t sc = a.scales[rr * (D / 16) + (lane >> 1)];
-                dequant8_hw(cw, sc, h);
+                const uint4 c4 = *reinterpret_cast<const uint4*>(a.codes + rr * (D / 2) + 64 * dw + 16 * sp);
+                const uint32_t sc = *reinterpret_cast<const uint16_t*>(a.scales + rr * (D / 16) + 8 * dw + 2 * sp);
+                dequant32_hw(c4, sc, h);
             } else if (slot < n_slots && slot - a.k < n_swa) {
                 valid = true;
                 const uint8_t* rp = swa_rows + static_cast<int64_t>(slot - a.k) * swa_row_bytes;
                 if (BF16) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(rp + 16 * lane);
-                    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        h[e] = pack_h2(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
+                    for (int e = 0; e < 4; ++e) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(rp + 2 * (128 * dw + 32 * sp + 8 * e));
+                        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            h[4 * e + j] = pack_h2(__uint_as_float(in[j] << 16), __uint_as_float(in[j] & 0xffff0000u));
+                    }
                 } else {
-                    const uint4 v0 = *reinterpret_cast<const uint4*>(rp + 32 * lane);
-                    const uint4 v1 = *reinterpret_cast<const uint4*>(rp + 32 * lane + 16);
-                    h[0] = pack_h2(__uint_as_float(v0.x), __uint_as_float(v0.y));
-                    h[1] = pack_h2(__uint_as_float(v0.z), __uint_as_float(v0.w));
-                    h[2] = pack_h2(__uint_as_float(v1.x), __uint_as_float(v1.y));
-                    h[3] = pack_h2(__uint_as_float(v1.z), __uint_as_float(v1.w));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float* fp = reinterpret_cast<const float*>(rp) + 128 * dw + 32 * sp + 8 * e;
+                        const uint4 v0 = *reinterpret_cast<const uint4*>(fp);
+                        const uint4 v1 = *reinterpret_cast<const uint4*>(fp + 4);
+                        h[4 * e] = pack_h2(__uint_as_float(v0.x), __uint_as_float(v0.y));
+                        h[4 * e + 1] = pack_h2(__uint_as_float(v0.z), __uint_as_float(v0.w));
+                        h[4 * e + 2] = pack_h2(__uint_as_float(v1.x), __uint_as_float(v1.y));
+                        h[4 * e + 3] = pack_h2(__uint_as_float(v1.z), __uint_as_float(v1.w));
+                    }
                 }
             }
-            store_key(buf, key, h, valid);
+            _Float16* dst = &Kt[buf][key * KROW + 128 * dw + 32 * sp];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                *reinterpret_cast<uint4*>(dst + 8 * e) = make_uint4(h[4 * e], h[4 * e + 1], h[4 * e + 2], h[4 * e + 3]);
+            if (dw == 0 && sp == 0) kmask[buf][key] = valid ? 0.0f : -__builtin_inff();
         }
     };
 
-    // ---- start-up.  First gathers (index entries from global memory),
-    // then the index window, then q.
-    if (n_it > 0 && is_main(0)) {
-        int32_t row[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int slot = tile_of(0) * KT + KPW * wv + 4 * g + gkey;
-            row[g] = slot < a.k ? idx[slot] : -1;
-        }
-        gather_rows(row);
-    }
-    stage_idx(t_begin);
+    // ---- start-up: the first main tile's rows (index entries straight
+    // from global memory), q staged in Kt[1] by all threads
+    if (!s_role && n_it > 0 && is_main(0)) gather_main(0);
     // q[u][hbase .. hbase + 63][0 .. 511] read once by all threads in 1 KiB
     // runs (thread t: 16-byte pieces t, t + 512, ...), staged as fp16 rows
     // of Kt[1] (the second tile buffer is free until phase 2 of the first
@@ -732,8 +765,6 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
                 qh[r][3] = pack_h2(__uint_as_float(v1.z), __uint_as_float(v1.w));
             }
         }
-        // the first tile, when it is a generic one, while q is in flight
-        if (n_it > 0 && !is_main(0)) load_generic(tile_of(0), 0);
 #pragma unroll
         for (int r = 0; r < QCH / 512; ++r) {
             const int c = tid + 512 * r;
@@ -745,8 +776,8 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             *reinterpret_cast<uint4*>(&Kt[1][(c >> 6) * KROW + 8 * (c & 63)]) = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
-    if (tid < 2) grow_s[tid] = 0;
-    __syncthreads();                                  // idx_s and q staged
+    if (tid < 4) pair_it[tid >> 1][tid & 1] = -1;
+    __syncthreads();                                  // q staged
 
     // ---- role registers: R holds the q fragments of an S-wave (32 k-steps
     // x 4 dwords) or the O^T accumulators of a D-wave (4 d tiles x 2 head
@@ -775,18 +806,19 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             R[st >> 2][4 * (st & 3) + 3] = __uint_as_float(v.w);
         }
     }
-    if (n_it > 0) {
-        if (is_main(0)) dequant_prefetched(0);
-        if (n_it > 1 && is_main(1)) prefetch_main(tile_of(1));
+    if (!s_role && n_it > 0) {
+        if (is_main(0)) dequant_slice(0);
+        else load_generic_slice(tile_of(0), 0);
+        if (n_it > 1 && is_main(1)) gather_main(1);
     }
     __syncthreads();                                  // first tile in Kt[0], q taken
 
     // O^T += V^T P^T for the tile in Kt[buf] with the P fragments in Pb
-    auto pv_tile = [&](int buf) {
-        if (grow_s[0] | grow_s[1]) {
+    auto pv_tile = [&](int buf) {        // buf: also the parity of its P, alpha and grow flags
+        if (grow_s[buf][0] | grow_s[buf][1]) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const float al = grow_s[nt] ? alpha_s[32 * nt + (lane & 31)] : 1.0f;
+                const float al = grow_s[buf][nt] ? alpha_s[buf][32 * nt + (lane & 31)] : 1.0f;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -796,8 +828,8 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
         const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const half8 pf0 = __builtin_bit_cast(half8, Pb[0][ks][lane]);
-            const half8 pf1 = __builtin_bit_cast(half8, Pb[1][ks][lane]);
+            const half8 pf0 = __builtin_bit_cast(half8, Pb[buf][0][ks][lane]);
+            const half8 pf1 = __builtin_bit_cast(half8, Pb[buf][1][ks][lane]);
             // A = V^T[32 d][16 k-slots]: k-slot 8h + i holds key
             // 16ks + 4h + (i % 4) + 8(i / 4), h = lane / 32 (the P order); the
             // transposed read hands lane 16g + i' the element i' % 4 of lanes
@@ -816,14 +848,16 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
                 R[2 * mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf0, R[2 * mt], 0, 0, 0);
                 R[2 * mt + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf1, R[2 * mt + 1], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);    // one k-step's fragments in registers at a time
         }
     };
 
-    for (int it = 0; it < n_it; ++it) {
-        const int buf = it & 1;
-        // ---------------- phase 1
-        float t2[16];
-        if (s_role) {
+    // one loop per role, so each role's registers are allocated on their own
+    // (the same number of barriers in both)
+    if (s_role) {
+        for (int it = 0; it < n_it; ++it) {
+            const int buf = it & 1;
+            float t2[16];
             // two independent accumulation chains (even / odd k-steps) keep
             // the matrix core busy across the dependent MFMA latency
             floatx16 s_acc, s_acc2;
@@ -855,17 +889,10 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, t2[r]);
             bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
             if (lane < 32) Lm[hg][kb][lane] = bmax;
-        } else if (it > 0) {
-            pv_tile(buf ^ 1);
-        }
-        __syncthreads();
-        // ---------------- phase 2
-        // index window for the main tile gathered at the end of this phase
-        if (it + 2 < n_it && is_main(it + 2) && tile_of(it + 2) - win0 >= kMaxTilesPerSplit) {
-            stage_idx(tile_of(it + 2));
-            __syncthreads();
-        }
-        if (s_role) {
+            // post this key half's maximum, then wait for the other half's
+            if (lane == 0) __hip_atomic_store(&pair_it[hg][kb], it, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            while (__hip_atomic_load(&pair_it[hg][kb ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != it)
+                __builtin_amdgcn_s_sleep(1);
             // tile max over both key blocks (same value in both S-waves of
             // the head group); the reference moves only when it is exceeded
             // by more than 8, so p < 2^8 and rescales are rare
@@ -880,8 +907,8 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
                 m_run = m_new;
             }
             if (kb == 0) {
-                if (lane < 32) alpha_s[32 * hg + lane] = al;
-                if (lane == 0) grow_s[hg] = any ? 1 : 0;
+                if (lane < 32) alpha_s[buf][32 * hg + lane] = al;
+                if (lane == 0) grow_s[buf][hg] = any ? 1 : 0;
             }
             uint32_t pk[8];
             float psum = 0.0f;
@@ -898,17 +925,34 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
                 }
             }
             l_run += psum;
-            Pb[hg][2 * kb][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            Pb[hg][2 * kb + 1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+            Pb[buf][hg][2 * kb][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            Pb[buf][hg][2 * kb + 1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+            __syncthreads();
         }
-        if (it + 1 < n_it) {
-            if (is_main(it + 1)) dequant_prefetched(buf ^ 1);
-            else load_generic(tile_of(it + 1), buf ^ 1);
-            if (it + 2 < n_it && is_main(it + 2)) prefetch_main(tile_of(it + 2));
+    } else {
+        // the iterations whose next tile is a window (generic) tile first,
+        // then those whose next tile is a main tile (from the registers the
+        // gather of two iterations before filled)
+        const int it_gen_end = n_gen < n_it ? n_gen : n_it;   // next tile generic for it + 1 < n_gen
+        int it = 0;
+        for (; it + 1 < it_gen_end; ++it) {
+            const int buf = it & 1;
+            if (it > 0) pv_tile(buf ^ 1);
+            load_generic_slice(tile_of(it + 1), buf ^ 1);
+            if (it + 2 < n_it && is_main(it + 2)) gather_main(it + 2);
+            __syncthreads();
         }
-        __syncthreads();
+        for (; it < n_it; ++it) {
+            const int buf = it & 1;
+            const bool next = it + 1 < n_it;
+            if (it > 0) pv_tile(buf ^ 1);
+            if (next) dequant_slice(buf ^ 1);
+            if (it + 2 < n_it) gather_main(it + 2);
+            __syncthreads();
+        }
+        if (n_it > 0) pv_tile((n_it - 1) & 1);
     }
-    if (!s_role && n_it > 0) pv_tile((n_it - 1) & 1);
+
 
     // ---------------- epilogue
     if (s_role) {
