@@ -11,12 +11,13 @@
 // Two kernels share the tile scheme (keys stream through LDS in tiles, the
 // dequantised tile is stored once key-major, and P.V reads it transposed
 // with ds_read_b64_tr_b16):
-//  * attn_kernel<D, NQ> (few query units; also D = 64): one workgroup =
+//  * attn_kernel<D, NQ> (D = 64): one workgroup =
 //    (unit, key split, block of 64 heads), 2*NQ waves; wave w owns head group
 //    hg = w & 1 and channel slice dq = w >> 1.  Per tile all waves gather and
 //    dequantise, form S^T over their channel slice (the NQ slices added
 //    through LDS), run the online softmax and add V^T P^T for their slice;
-//  * attn_ws_kernel (D = 512, many units): warp-specialised, see there.
+//  * attn_ws_kernel (D = 512, any number of units): warp-specialised, see
+//    there.
 // Common to both:
 //  - S^T[key][head] with v_mfma_f32_32x32x16_f16 (A = key rows, B = q);
 //  - online softmax in base 2 with a lazy reference: p = exp2(t - m_ref),
@@ -1150,7 +1151,10 @@ SplitPlan plan(int64_t units, int H, int k, int W, int KT) {
 // write-out) plus the combine's reading of the partials.  Fixed at the
 // MI355X CU count, so the workspace size never depends on the device.
 constexpr int kCUs = 256;
-bool use_ws(int64_t units, int D) { return D == 512 && units >= 16; }
+// D = 512 always takes the warp-specialised kernel (at 4, 8 and 12 units
+// too: 22.6, 24.6 and 26.8 us against 24.8, 27.1 and 29.2 us for the split
+// kernel, attention and combine together); D = 64 the split kernel.
+constexpr bool use_ws(int D) { return D == 512; }
 
 SplitPlan plan_ws(int64_t units, int H, int k, int W, int KT) {
     SplitPlan best;
@@ -1182,8 +1186,8 @@ SplitPlan plan_ws(int64_t units, int H, int k, int W, int KT) {
 
 template <int D, int NQ, bool BF16>
 hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
-    const SplitPlan sp = use_ws(L.units, D) ? plan_ws(L.units, L.H, L.k, L.W, tile_keys(D))
-                                            : plan(L.units, L.H, L.k, L.W, tile_keys(D));
+    const SplitPlan sp = use_ws(D) ? plan_ws(L.units, L.H, L.k, L.W, tile_keys(D))
+                                    : plan(L.units, L.H, L.k, L.W, tile_keys(D));
     const int hblocks = (L.H + 63) / 64;
     AttnArgs a;
     a.q = static_cast<const uint16_t*>(L.q); a.q_bf16 = L.q_bf16;
@@ -1198,12 +1202,7 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     a.ws_m = L.ws ? L.ws + nparts * 64 * D : nullptr;
     a.ws_l = L.ws ? a.ws_m + nparts * 64 : nullptr;
     if (L.units == 0) return hipSuccess;
-    // 16 or more query units (prefill chunks, decode batches of 16+): the
-    // warp-specialised kernel keeps the matrix cores busier (MI355X, 64
-    // heads, k = 2048: 28.8 against 42.0 us at 16 units, 39.4 against 56.4 us
-    // at 32); at 8 units the split kernel's shorter start-up wins (23.4
-    // against 24.7 us)
-    if (use_ws(L.units, D)) {
+    if constexpr (use_ws(D)) {
         const dim3 grid(static_cast<unsigned>(L.units), sp.splits, hblocks);
         if (L.cap * (D / 2) <= 0x7fffffffLL)
             attn_ws_kernel<BF16, true><<<grid, 512, 0, st>>>(a);
@@ -1230,7 +1229,7 @@ bool attn_shape_supported(int H, int D) {
 }
 
 size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W) {
-    const SplitPlan sp = use_ws(units, D) ? plan_ws(units, H, k, W, tile_keys(D)) : plan(units, H, k, W, tile_keys(D));
+    const SplitPlan sp = use_ws(D) ? plan_ws(units, H, k, W, tile_keys(D)) : plan(units, H, k, W, tile_keys(D));
     if (sp.splits == 1) return 0;
     const int64_t hblocks = (H + 63) / 64;
     const int64_t nparts = units * hblocks * sp.splits;
