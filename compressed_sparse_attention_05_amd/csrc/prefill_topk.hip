@@ -280,7 +280,6 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     int32_t lim[2][2];
     float thf[2][2];
     float* sbase[2][2];
-    uint32_t coff[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -293,7 +292,6 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
             lim[mt][e] = static_cast<int32_t>(v - (lane & 31));
             thf[mt][e] = SAMPLE ? 0.0f : thr_float(thr[tc - t0]);
             sbase[mt][e] = SAMPLE ? samp + (tc - t0) * ld_s + (lane & 31) : nullptr;
-            coff[mt][e] = static_cast<uint32_t>(((4 * mt + (hi ? 2 + e : e)) * g.cand_ld + bx * (kSub * g.blocks)) * 8);
         }
     // the wave's 8 candidate rows as one buffer (byte range below 2^31,
     // which the launch checks; rows past the chunk are outside the range)
@@ -302,10 +300,14 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
         SAMPLE ? static_cast<void*>(samp) : static_cast<void*>(cand + (qb < t1 ? qb - t0 : 0) * g.cand_ld),
         static_cast<short>(0), SAMPLE ? 0 : static_cast<int>(rows_here * g.cand_ld * 8), 0x00020000);
-    // uniform count of candidates emitted so far per wave row (4mt + query)
-    uint32_t c_glob[8];
+    // uniform slot of the next candidate of wave row q (4mt + query) in the
+    // wave's buffer: q * cand_ld + the workgroup's first slot + the count so far
+    const uint32_t slot0 = static_cast<uint32_t>(bx * (kSub * g.blocks));
+    uint32_t c_pos[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) c_glob[q] = 0;
+    for (int q = 0; q < 8; ++q) c_pos[q] = static_cast<uint32_t>(q * g.cand_ld) + slot0;
+    uint32_t hmask = hi ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(hmask));    // keep the masked xor below from becoming a select
 
     // tile loader: thread -> chunk c = tid / 32 of key (tid % 32) in each of
     // the tile's 4 column blocks.  Consecutive candidate tiles are 128 keys
@@ -380,22 +382,28 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
                     // the wave holds row qlo, the upper half row qhi.  Lanes
                     // that take nothing store past the buffer's range, which
                     // the hardware drops, so the store needs no branch.
-                    const bool take = vis_ok && v >= thf[mt][e];
-                    const uint64_t bal = __ballot(take);
+                    // an invisible key compares as NaN, so the ballot is one compare
+                    const float vt = vis_ok ? v : __builtin_nanf("");
+                    const bool take = vt >= thf[mt][e];
+                    const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
                     const uint32_t blo = static_cast<uint32_t>(bal), bhi = static_cast<uint32_t>(bal >> 32);
                     const uint32_t n_lo = static_cast<uint32_t>(__builtin_popcount(blo));
                     const uint32_t n_hi = static_cast<uint32_t>(__builtin_popcount(bhi));
                     const int qlo = 4 * mt + e, qhi = 4 * mt + 2 + e;
-                    const uint32_t base = hi ? c_glob[qhi] - n_lo : c_glob[qlo];
+                    // the upper lanes' prefix count includes the n_lo lower
+                    // lanes, so their base is lowered by n_lo; the select of
+                    // the two uniform bases is a masked xor
+                    const uint32_t x = c_pos[qlo] ^ (c_pos[qhi] - n_lo);
+                    const uint32_t base = c_pos[qlo] ^ (x & hmask);
                     const uint32_t at = __builtin_amdgcn_mbcnt_hi(bhi, __builtin_amdgcn_mbcnt_lo(blo, base));
                     // (every real offset is below 2^31; bit 31 marks the rest)
-                    const uint32_t off = (coff[mt][e] + 8u * at) | (static_cast<uint32_t>(!take) << 31);
+                    const uint32_t off = (at << 3) | (static_cast<uint32_t>(!take) << 31);
                     u32x2 val;
                     val[0] = __float_as_uint(v);
                     val[1] = static_cast<uint32_t>(jb32) + (lane & 31);
                     __builtin_amdgcn_raw_buffer_store_b64(val, crsrc, static_cast<int>(off), 0, 0);
-                    c_glob[qlo] += n_lo;
-                    c_glob[qhi] += n_hi;
+                    c_pos[qlo] += n_lo;
+                    c_pos[qhi] += n_hi;
                 }
             }
         }
@@ -414,13 +422,16 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
             __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);    // VALU
         }
     };
+    // tile t + 1 is loaded into registers a whole tile ahead (before the last
+    // block's candidate stores of tile t - 1), so the wait before its LDS
+    // write covers only stores issued a tile earlier
     load_tile(0);
     store_tile(0);
+    if (n_tiles > 1) load_tile(1);
     __syncthreads();
     mfma_block(0, 0, acc0);
     for (int tile = 0; tile < n_tiles; ++tile) {
         const int buf = tile & 1;
-        if (tile + 1 < n_tiles) load_tile(tile + 1);
         mfma_block(buf, 1, acc1);
         epilogue(acc0, 4 * tile + 0);
         interleave();
@@ -431,6 +442,7 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
         epilogue(acc0, 4 * tile + 2);
         interleave();
         if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+        if (tile + 2 < n_tiles) load_tile(tile + 2);
         __syncthreads();
         if (tile + 1 < n_tiles) mfma_block(buf ^ 1, 0, acc0);
         epilogue(acc1, 4 * tile + 3);
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     if (!SAMPLE && lane < 8) {
         uint32_t c = 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) c = lane == q ? c_glob[q] : c;
+        for (int q = 0; q < 8; ++q) c = lane == q ? c_pos[q] - static_cast<uint32_t>(q * g.cand_ld) - slot0 : c;
         const int64_t t = qb + lane;
         if (t < t1) counts[(t - t0) * g.cnt_ld + bx] = c;
     }
