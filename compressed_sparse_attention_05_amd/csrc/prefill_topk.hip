@@ -48,6 +48,8 @@
 // Launch shape: the scoring grids are sized to whole rounds of one
 // workgroup per CU, and numbered so the workgroups that read the same keys
 // share an XCD's L2.
+#include <type_traits>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -67,7 +69,7 @@ constexpr int kChunkRows = 1024;               // query rows per scratch chunk
 constexpr int kQB = 64;                        // queries per scoring workgroup
 constexpr int kSub = 32;                       // keys per MFMA column block
 constexpr int kTileKeys = 128;                 // keys per LDS tile (4 column blocks)
-constexpr int kMaxKeysPerWG = 8192;            // largest key range of a candidate workgroup
+constexpr int kMaxKeysPerWG = 16384;            // largest key range of a candidate workgroup
 constexpr int kGroup = 512;                    // sample: one 32-key block per 512 keys
 constexpr float kEpsRel = 4.0e-5f;
 
@@ -315,11 +317,24 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     // constant; a tile reaching past the cache clamps per key.
     const int lc = tid >> 5, lk = tid & 31;
     uint4 n0, n1, n2, n3;
+    // candidate pass: the workgroup's keys [kbase, cap) of the cache as one
+    // buffer (reads past it return 0; such keys are never visible), chunk lc
+    // of key lk at voff within a 64-key cache tile, the tile's four column
+    // blocks at uniform offsets
+    const int64_t kbase = SAMPLE ? 0 : bx * g.blocks * kSub;
+    int64_t krem = SAMPLE ? 0 : (a.cap - kbase) * (kNch * 16);
+    krem = krem < 0 ? 0 : (krem > 0x7fffffffLL ? 0x7fffffffLL : krem);
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.kc) + (SAMPLE ? 0 : kbase * (kNch * 16)), static_cast<short>(0),
+        static_cast<int>(krem), 0x00020000);
+    const int voff = (lc * 64 + lk) * 16;
     auto load_tile = [&](int tile) {
-        const int64_t kb0 = block_key(4 * tile);
-        if (!SAMPLE && kb0 + kTileKeys <= a.cap) {
-            const uint4* p = kchunk(a.kc, kb0 + lk, lc);        // +32 keys = +32 entries; +64 keys = next cache tile
-            n0 = p[0]; n1 = p[32]; n2 = p[kNch * 64]; n3 = p[kNch * 64 + 32];
+        if (!SAMPLE) {
+            const int so = tile * (2 * kNch * 64 * 16);   // two cache tiles per candidate tile
+            n0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, voff, so, 0));
+            n1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, voff, so + 32 * 16, 0));
+            n2 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, voff, so + kNch * 64 * 16, 0));
+            n3 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, voff, so + (kNch * 64 + 32) * 16, 0));
         } else {
             int64_t p0 = block_key(4 * tile + 0) + lk, p1 = block_key(4 * tile + 1) + lk;
             int64_t p2 = block_key(4 * tile + 2) + lk, p3 = block_key(4 * tile + 3) + lk;
@@ -354,7 +369,10 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     // s~ of column block b (keys from jb) and what becomes of it; every block
     // is computed (loads of keys past the end read row 0) and invisible keys
     // are masked here
-    auto epilogue = [&](const floatx16* acc, int b) {
+    // VIS false: every key of the block is visible to every row of the wave,
+    // so no key needs the visibility test
+    auto epilogue = [&](const floatx16* acc, int b, auto vis_tag) {
+        constexpr bool VIS = decltype(vis_tag)::value;
         const int64_t jb = block_key(b);
         const int32_t jb32 = static_cast<int32_t>(jb < 0x7fffffff ? jb : 0x7fffffff);
 #pragma unroll
@@ -372,7 +390,7 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[e]),
                                                                  __float_as_uint(part[2 + e]), false, false);
                 const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                const bool vis_ok = jb32 < lim[mt][e];
+                const bool vis_ok = !VIS || jb32 < lim[mt][e];
                 if (SAMPLE) {
                     const int64_t gi = jb / kGroup;
                     if (gi * kSub < ld_s) sbase[mt][e][gi * kSub] = vis_ok ? v : -__builtin_inff();
@@ -430,23 +448,37 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     if (n_tiles > 1) load_tile(1);
     __syncthreads();
     mfma_block(0, 0, acc0);
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    // the smallest visible count of the wave's rows (0 if a row lies past the
+    // chunk): vis grows with t, so it is the first row's
+    int64_t min_vis = qb + 7 < t1 ? vis_of(a, qb) : 0;
+    if (min_vis > n_cols) min_vis = n_cols;
+    auto tile_body = [&](int tile, auto vis_tag) {
         const int buf = tile & 1;
         mfma_block(buf, 1, acc1);
-        epilogue(acc0, 4 * tile + 0);
+        epilogue(acc0, 4 * tile + 0, vis_tag);
         interleave();
         mfma_block(buf, 2, acc0);
-        epilogue(acc1, 4 * tile + 1);
+        epilogue(acc1, 4 * tile + 1, vis_tag);
         interleave();
         mfma_block(buf, 3, acc1);
-        epilogue(acc0, 4 * tile + 2);
+        epilogue(acc0, 4 * tile + 2, vis_tag);
         interleave();
         if (tile + 1 < n_tiles) store_tile(buf ^ 1);
         if (tile + 2 < n_tiles) load_tile(tile + 2);
         __syncthreads();
         if (tile + 1 < n_tiles) mfma_block(buf ^ 1, 0, acc0);
-        epilogue(acc1, 4 * tile + 3);
+        epilogue(acc1, 4 * tile + 3, vis_tag);
+    };
+    // keys grow with the tile index: the leading tiles whose last key is
+    // below min_vis run without the test, the rest with it
+    int n_fast = 0;
+    if (!SAMPLE) {
+        const int64_t f = (min_vis / kSub - bx * g.blocks) / 4;
+        n_fast = static_cast<int>(f < 0 ? 0 : (f > n_tiles ? n_tiles : f));
     }
+    int tile = 0;
+    for (; tile < n_fast; ++tile) tile_body(tile, std::false_type{});
+    for (; tile < n_tiles; ++tile) tile_body(tile, std::true_type{});
     if (!SAMPLE && lane < 8) {
         uint32_t c = 0;
 #pragma unroll
@@ -909,7 +941,7 @@ hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st)
         sample_thresh_kernel<<<dim3(static_cast<unsigned>(rows)), kThreads, 0, st>>>(t0, a, w.samp, w.ld_s, w.thr);
         int64_t kpw = kTileKeys;
         if (cols > 0) {
-            Geo gc = make_geo(cdiv(cols, kSub), qblocks, 4096 / kSub, kMaxKeysPerWG / kSub, n_cu);
+            Geo gc = make_geo(cdiv(cols, kSub), qblocks, 8192 / kSub, kMaxKeysPerWG / kSub, n_cu);
             gc.cand_ld = w.cand_ld;
             if (8 * 8 * w.cand_ld > 0x7fffffffLL) return hipErrorInvalidValue;
             gc.cnt_ld = w.cnt_ld;
