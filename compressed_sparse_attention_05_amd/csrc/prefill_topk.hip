@@ -22,20 +22,23 @@
 //     norms themselves.
 //  2. Sample.  s~ of one 32-key block in every 512 keys (the block picked by
 //     a hash of the group, so periodic structure cannot alias) gives each row a
-//     lower key L_t: the sample's j-th largest, j chosen so that about 3k
-//     keys of the whole row are expected at or above it.
+//     lower key L_t: the lower edge of the radix bin that holds the sample's
+//     j-th largest, j chosen so that about 3k keys of the whole row are
+//     expected at or above it.
 //  3. Candidates.  The full matrix-core pass keeps (s~, position) of every
 //     key with s~ >= L_t; each workgroup owns a fixed slot range per row
 //     (as many slots as it has keys), so no atomics are needed.
 //  4. Final, per row: with C candidates, k <= C and tau~ the k-th largest
 //     candidate s~ (then also the k-th of the whole row, since every other
-//     key lies below L_t), the check L_t <= tau~ - 2 eps shows that every key
-//     within 2 eps of tau~ or above is a candidate.  Then s~ > tau~ + 2 eps
-//     => s > tau (chosen), s~ < tau~ - 2 eps => s < tau (not chosen), where
-//     tau is the exact k-th score; keys in between are rescored with the
-//     exact chain and fill the remaining slots by (exact score desc,
-//     position asc).  Every key whose exact score equals tau lies in that
-//     band, so ties resolve exactly as in the definition.
+//     key lies below L_t), one radix pass over the candidates gives a bin
+//     [lo, hi] that holds tau~.  The exact k-th score tau then lies in
+//     [lo - eps, hi + eps].  The check L_t <= lo - 2 eps shows that every key
+//     within 2 eps of the bin or above is a candidate.  Then s~ > hi + 2 eps
+//     => s > tau (chosen), s~ < lo - 2 eps => s < tau (not chosen); keys in
+//     between (the band) are rescored with the exact chain and fill the
+//     remaining slots by (exact score desc, position asc).  Every key whose
+//     exact score equals tau lies in the band, so ties resolve exactly as in
+//     the definition.
 //
 // A row that fails a check (too few or too many candidates, a band wider
 // than the fixed LDS budget) is rescored exactly over its whole row and
@@ -536,8 +539,10 @@ __global__ __launch_bounds__(kThreads) void sample_thresh_kernel(int64_t t0, PfA
         uint32_t mn, mx;
         const uint32_t n_s = sel_stats<kSampPerThread>(kk, sh, mn, mx);
         if (n_s > 0) {
-            uint32_t need = rank_of(n_s);
-            T = sel_passes<kSampPerThread, false>(kk, mn, mx, need, sh);
+            // L_t: the lower edge of the radix bin that holds the j-th
+            // largest sample (at least j samples lie at or above it)
+            uint32_t need = rank_of(n_s), hi_unused;
+            sel_bracket<kSampPerThread>(kk, mn, mx, need, sh, T, hi_unused);
         }
     } else {
         auto get = [&](int64_t i) { return key_of(s[i]); };
@@ -646,8 +651,10 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
     const int64_t n_seg = (vis + kpw - 1) / kpw;   // workgroups that saw visible keys
 
     // total candidates
-    uint32_t part = 0;
-    for (int64_t sgi = tid; sgi < n_seg; sgi += kThreads) part += crow[sgi];
+    // (the first kThreads counts stay in registers for the gather)
+    const uint32_t cnt0 = tid < n_seg ? crow[tid] : 0u;
+    uint32_t part = cnt0;
+    for (int64_t sgi = tid + kThreads; sgi < n_seg; sgi += kThreads) part += crow[sgi];
     part = wave_sum(part);
     if (lane == 0) wave_tot[wv] = part;
     __syncthreads();
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
         uint32_t running = 0;
         for (int64_t sb = 0; sb < n_seg; sb += kThreads) {
             const int64_t sgi = sb + tid;
-            const uint32_t c = sgi < n_seg ? crow[sgi] : 0u;
+            const uint32_t c = sb == 0 ? cnt0 : (sgi < n_seg ? crow[sgi] : 0u);
             const uint32_t incl = wave_incl_sum(c);
             if (lane == 63) wave_tot[wv] = incl;
             __syncthreads();
@@ -678,10 +685,22 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
             for (int s = wv; s < n_here; s += kWaves) {
                 const uint32_t so = hist[s], sc = hist[1024 + s];
                 const uint2* src = region + (sb + s) * kpw;
-                for (uint32_t i = lane; i < sc; i += 64) {
-                    const uint2 cv = src[i];
-                    ckey[so + i] = cv.x;
-                    cpos[so + i] = cv.y;
+                // eight loads in flight per lane, then their LDS writes
+                for (uint32_t i0 = 0; i0 < sc; i0 += 64 * 8) {
+                    uint2 cv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t i = i0 + lane + 64 * u;
+                        if (i < sc) cv[u] = src[i];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t i = i0 + lane + 64 * u;
+                        if (i < sc) {
+                            ckey[so + i] = cv[u].x;
+                            cpos[so + i] = cv[u].y;
+                        }
+                    }
                 }
             }
             running += tot;
@@ -696,12 +715,13 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
             kk[j] = i < C ? key_of(__uint_as_float(ckey[i])) : 0u;
         }
         __syncthreads();
-        // tau~: the k-th largest s~ (of the candidates, and of the row)
-        uint32_t T;
+        // [T_lo, T_hi]: one radix bin that holds tau~, the k-th largest s~ (of
+        // the candidates, and of the row)
+        uint32_t T_lo, T_hi;
         {
             uint32_t mn, mx, need = k_eff;
             sel_stats<kCandPerThread>(kk, u_lds.sh, mn, mx);
-            T = sel_passes<kCandPerThread, false>(kk, mn, mx, need, u_lds.sh);
+            sel_bracket<kCandPerThread>(kk, mn, mx, need, u_lds.sh, T_lo, T_hi);
         }
         __syncthreads();
 #pragma unroll
@@ -710,10 +730,9 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
             if (i < C) ckey[i] = kk[j];
         }
         __syncthreads();
-        const float tau = float_of_key(T);
         const float e2 = 2.0f * eps[t];
-        const uint32_t hi_key = key_of(next_up(tau + e2));
-        const uint32_t lo_raw = key_of(next_down(tau - e2));
+        const uint32_t hi_key = key_of(next_up(float_of_key(T_hi) + e2));
+        const uint32_t lo_raw = key_of(next_down(float_of_key(T_lo) - e2));
         const uint32_t lo_key = lo_raw > 0u ? lo_raw : 1u;
         if (tid < 2) counters[tid] = 0;
         __syncthreads();
@@ -722,15 +741,18 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
         } else {
             // sure picks (s~ above the band) are counted; band keys go to
             // band[] as candidate indices
+            uint32_t n_sure = 0;
             for (uint32_t i = tid; i < C; i += kThreads) {
                 const uint32_t ck = ckey[i];
                 if (ck > hi_key) {
-                    atomicAdd(&counters[0], 1u);
+                    ++n_sure;
                 } else if (ck >= lo_key) {
                     const uint32_t at = atomicAdd(&counters[1], 1u);
                     if (at < static_cast<uint32_t>(kBandCap)) band[at] = i;
                 }
             }
+            n_sure = wave_sum(n_sure);
+            if (lane == 0) atomicAdd(&counters[0], n_sure);
             __syncthreads();
             const uint32_t n_in = counters[0], n_band = counters[1];
             if (n_band > static_cast<uint32_t>(kBandCap) || n_in > k_eff || n_in + n_band < k_eff) {
@@ -771,14 +793,19 @@ __global__ __launch_bounds__(kThreads) void cand_final_kernel(int64_t t0, PfArgs
                 }
                 __syncthreads();
                 // ordered emission: candidates are in position order
-                uint32_t written = 0;
-                for (uint32_t base = 0; base < C; base += kThreads) {
-                    const uint32_t i = base + tid;
-                    const bool pick = i < C && ckey[i] > hi_key;
-                    uint32_t tot;
-                    const uint32_t at = written + block_excl_prefix(pick, wave_tot, tot);
-                    if (pick && at < k_eff) o[at] = static_cast<int32_t>(cpos[i]);
-                    written += tot;
+                // (thread tid owns candidates [tid * per, (tid + 1) * per),
+                // so one workgroup scan orders every pick)
+                const uint32_t per = (C + kThreads - 1) / kThreads;
+                const uint32_t c0 = tid * per, c1 = c0 + per < C ? c0 + per : C;
+                uint32_t mine = 0;
+                for (uint32_t i = c0; i < c1; ++i) mine += ckey[i] > hi_key ? 1u : 0u;
+                uint32_t tot;
+                uint32_t at = block_excl_scan(mine, wave_tot, tot);
+                for (uint32_t i = c0; i < c1; ++i) {
+                    if (ckey[i] > hi_key) {
+                        if (at < k_eff) o[at] = static_cast<int32_t>(cpos[i]);
+                        ++at;
+                    }
                 }
             }
         }

@@ -341,13 +341,15 @@ __device__ __forceinline__ uint32_t sel_stats(const uint32_t (&kk)[R], SelLds& s
 // high bits are counted as above when larger, which the caller has already
 // subtracted from need, or are never chosen when smaller).  hist[0] must be
 // clear.
-template <int R, bool EARLY = false>
+// MAXP: stop after that many passes; *rem_bits (when given) is then the
+// number of low bits still unresolved below the returned prefix.
+template <int R, bool EARLY = false, int MAXP = 32>
 __device__ __forceinline__ uint32_t sel_passes_from(const uint32_t (&kk)[R], int top, uint64_t known, uint32_t& need,
-                                                    SelLds& sh) {
+                                                    SelLds& sh, int* rem_bits = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int hb = kSelBins - 8 - 8 * tid;         // this thread's bins
     int buf = 0;
-    while (top >= 0) {
+    for (int pass = 0; top >= 0 && pass < MAXP; ++pass) {
         const int nb = top + 1 < kSelBits ? top + 1 : kSelBits;
         const int shift = top + 1 - nb;
         const uint32_t dmask = (1u << nb) - 1u;
@@ -428,6 +430,7 @@ __device__ __forceinline__ uint32_t sel_passes_from(const uint32_t (&kk)[R], int
         top = shift - 1;
         buf ^= 1;
     }
+    if (rem_bits) *rem_bits = top + 1;
     return static_cast<uint32_t>(known);
 }
 
@@ -437,6 +440,20 @@ __device__ __forceinline__ uint32_t sel_passes(const uint32_t (&kk)[R], uint32_t
     if (mn == mx) return mn;                       // every nonempty key is T
     const int top = 31 - __builtin_clz(mn ^ mx);   // highest bit not shared
     return sel_passes_from<R, EARLY>(kk, top, static_cast<uint64_t>(mn) >> (top + 1), need, sh);
+}
+
+// One histogram pass: on return the need-th largest key lies in [lo, hi]
+// (lo == hi when every bit is resolved), and need is its rank among the keys
+// of that range.
+template <int R>
+__device__ __forceinline__ void sel_bracket(const uint32_t (&kk)[R], uint32_t mn, uint32_t mx, uint32_t& need,
+                                            SelLds& sh, uint32_t& lo, uint32_t& hi) {
+    if (mn == mx) { lo = hi = mn; return; }
+    const int top = 31 - __builtin_clz(mn ^ mx);
+    int rem = 0;
+    const uint32_t p = sel_passes_from<R, false, 1>(kk, top, static_cast<uint64_t>(mn) >> (top + 1), need, sh, &rem);
+    lo = rem >= 32 ? 0u : p << rem;
+    hi = rem >= 32 ? 0xffffffffu : (lo | ((1u << rem) - 1u));
 }
 
 // Stage 3, ordered emission of the keys above T plus the first `need` keys
