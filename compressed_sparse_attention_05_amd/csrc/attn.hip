@@ -59,7 +59,9 @@ struct AttnArgs {
     int64_t units; int H;
     float c2;                                // sm_scale * log2(e)
     float* out;
-    float* ws_o; float* ws_m; float* ws_l;   // partials (splits > 1)
+    // partials (splits > 1): each split's output divided by its own row sum,
+    // as fp16, and its row max and row sum as fp32
+    _Float16* ws_o; float* ws_m; float* ws_l;
     int splits, tiles_per_split, n_tiles;
 };
 
@@ -518,11 +520,13 @@ __global__ __launch_bounds__(128 * NQ) void attn_kernel(AttnArgs a) {
         }
     } else {
         const int64_t pidx = (u * gridDim.z + hb) * a.splits + split;
-        float* po = a.ws_o + pidx * (64 * D);
+        _Float16* po = a.ws_o + pidx * (64 * D);
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) po[((wv * MT + mt) * 16 + r) * 64 + lane] = o_acc[mt][r];
+            for (int r = 0; r < 16; ++r)
+                po[((wv * MT + mt) * 16 + r) * 64 + lane] = static_cast<_Float16>(o_acc[mt][r] * inv);
         if (dq == 0 && lane < 32) {
             a.ws_m[pidx * 64 + head_local] = m_run;
             a.ws_l[pidx * 64 + head_local] = l_tot;
@@ -988,14 +992,16 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
     } else {
         // partial layout of combine_kernel<512, 4>: block (w' = 2dw + nt, mt)
         const int64_t pidx = (u * gridDim.z + hb) * a.splits + split;
-        float* po = a.ws_o + pidx * (64 * D);
+        _Float16* po = a.ws_o + pidx * (64 * D);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt) {
+            const float inv = l_tot[nt] > 0.0f ? 1.0f / l_tot[nt] : 0.0f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    po[(((2 * dw + nt) * 4 + mt) * 16 + r) * 64 + lane] = R[2 * mt + nt][r];
+                    po[(((2 * dw + nt) * 4 + mt) * 16 + r) * 64 + lane] = static_cast<_Float16>(R[2 * mt + nt][r] * inv);
+        }
         if (dw == 0 && lane < 32) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
@@ -1015,7 +1021,7 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
 // Reads are in the partials' own (coalesced) order; each result block is
 // transposed through LDS so the output rows are written as 128-byte runs.
 template <int D, int NQ>
-__global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ ws_o,
+__global__ __launch_bounds__(1024) void combine_kernel(const _Float16* __restrict__ ws_o,
                                                        const float* __restrict__ ws_m,
                                                        const float* __restrict__ ws_l, int splits,
                                                        int H, int hblocks, int bpw, float* __restrict__ out) {
@@ -1030,7 +1036,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
     const int hcol = ln & 31;
     const int dd = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
     constexpr int64_t PS = 64 * D;                 // partial stride
-    const float* pbase = ws_o + ub * splits * static_cast<int64_t>(64 * D);
+    const _Float16* pbase = ws_o + ub * splits * static_cast<int64_t>(64 * D);
     const int hb = static_cast<int>(ub % hblocks);
     const int64_t u = ub / hblocks;
     const int oh = t >> 5, od = t & 31;
@@ -1046,18 +1052,22 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
     // them; otherwise the first block's first 16 splits.
     const bool all16 = bpw == 4 && splits <= 4;
     constexpr int kEarly = 16;
-    float oe[kEarly];
+    // raw 16-bit loads, one per register and widened where used, so no wait
+    // follows the loads
+    uint32_t oe[kEarly];
+    auto h2f = [](uint32_t x) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x))); };
     if (all16) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const float* po = block_ptr(j0 + jj);
+            const _Float16* po = block_ptr(j0 + jj);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) oe[4 * jj + s] = s < splits ? po[s * PS] : 0.0f;
+            for (int s = 0; s < 4; ++s)          // (unconditional loads of a clamped split)
+                oe[4 * jj + s] = *reinterpret_cast<const uint16_t*>(po + (s < splits ? s : splits - 1) * PS);
         }
     } else {
-        const float* po = block_ptr(j0);
+        const _Float16* po = block_ptr(j0);
 #pragma unroll
-        for (int i = 0; i < kEarly; ++i) oe[i] = i < splits ? po[i * PS] : 0.0f;
+        for (int i = 0; i < kEarly; ++i) oe[i] = *reinterpret_cast<const uint16_t*>(po + (i < splits ? i : splits - 1) * PS);
     }
     // per-head split weights, once per workgroup: thread t loads (split
     // t/32, head 32hg + t%32), then thread t < 32 reduces over the splits
@@ -1077,7 +1087,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
         for (int s = 0; s < splits; ++s) {
             const float ms = wgt[s][t];
             const float w = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mstar);
-            wgt[s][t] = w;
+            // a split's partial is its output divided by its row sum
+            wgt[s][t] = w * lsum[s][t];
             den += w * lsum[s][t];
         }
         inv_den[t] = den > 0.0f ? 1.0f / den : 0.0f;
@@ -1095,29 +1106,29 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
         for (int jj = 0; jj < 4; ++jj) {
             float num = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) num += s < splits ? wgt[s][hcol] * oe[4 * jj + s] : 0.0f;
+            for (int s = 0; s < 4; ++s) num += s < splits ? wgt[s][hcol] * h2f(oe[4 * jj + s]) : 0.0f;
             emit(j0 + jj, num, jj == 0);
         }
         return;
     }
     for (int jj = 0; jj < bpw; ++jj) {
         const int j = j0 + jj;
-        const float* po = block_ptr(j);
+        const _Float16* po = block_ptr(j);
         float num = 0.0f;
         int s = 0;
         if (jj == 0) {
 #pragma unroll
-            for (int i = 0; i < kEarly; ++i) num += i < splits ? wgt[i][hcol] * oe[i] : 0.0f;
+            for (int i = 0; i < kEarly; ++i) num += i < splits ? wgt[i][hcol] * h2f(oe[i]) : 0.0f;
             s = kEarly;
         }
         for (; s + 8 <= splits; s += 8) {
             float o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = po[(s + i) * PS];
+            for (int i = 0; i < 8; ++i) o[i] = static_cast<float>(po[(s + i) * PS]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) num += wgt[s + i][hcol] * o[i];
         }
-        for (; s < splits; ++s) num += wgt[s][hcol] * po[s * PS];
+        for (; s < splits; ++s) num += wgt[s][hcol] * static_cast<float>(po[s * PS]);
         emit(j, num, jj == 0);
     }
 }
@@ -1198,8 +1209,9 @@ hipError_t launch_d(const AttnLaunch& L, hipStream_t st) {
     a.units = L.units; a.H = L.H; a.c2 = L.sm_scale * kLog2e; a.out = L.out;
     a.splits = sp.splits; a.tiles_per_split = sp.tiles_per_split; a.n_tiles = sp.n_tiles;
     const int64_t nparts = L.units * hblocks * sp.splits;
-    a.ws_o = L.ws;
-    a.ws_m = L.ws ? L.ws + nparts * 64 * D : nullptr;
+    // [nparts][64][D] fp16 partials, then [nparts][64] row maxima and sums
+    a.ws_o = reinterpret_cast<_Float16*>(L.ws);
+    a.ws_m = L.ws ? reinterpret_cast<float*>(reinterpret_cast<char*>(L.ws) + nparts * 64 * D * sizeof(_Float16)) : nullptr;
     a.ws_l = L.ws ? a.ws_m + nparts * 64 : nullptr;
     if (L.units == 0) return hipSuccess;
     if constexpr (use_ws(D)) {
@@ -1233,7 +1245,7 @@ size_t attn_workspace_bytes(int64_t units, int H, int D, int k, int W) {
     if (sp.splits == 1) return 0;
     const int64_t hblocks = (H + 63) / 64;
     const int64_t nparts = units * hblocks * sp.splits;
-    return static_cast<size_t>(nparts) * (64 * static_cast<size_t>(D) + 128) * sizeof(float);
+    return static_cast<size_t>(nparts) * (64 * static_cast<size_t>(D) * sizeof(_Float16) + 128 * sizeof(float));
 }
 
 hipError_t launch_attn(const AttnLaunch& L, hipStream_t st) {
