@@ -353,9 +353,10 @@ int csa2_sparse_attn_prefill(const csa2_attn_prefill_args *a, void *ws, size_t w
  *          cap rows (cap % 64 == 0), bf16
  *   out_idx [T][k] int32: min(k, vis(t)) ascending positions, then -1.
  * 1 <= k <= 4096 and vis(T-1) <= 2^24 (CSA2_E_UNSUPPORTED beyond).  Inputs
- * must be finite with scores far from float32 overflow.  Workspace: csa2_prefill_topk_workspace_size (about
- * 4 * min(T, 1024) * vis(T-1) bytes of approximate scores plus 100 KB per
- * row of that chunk); 256-byte aligned.
+ * must be finite with scores far from float32 overflow.  Workspace:
+ * csa2_prefill_topk_workspace_size, 256-byte aligned: per row of a chunk of
+ * min(T, 1024) rows, about 8.3 * vis(T-1) bytes of candidate slots, sample
+ * scores and counts, plus 128 KiB.
  * ------------------------------------------------------------------------ */
 typedef struct csa2_prefill_topk_args {
     const void *q_idx;  int32_t q_dtype;  /* [T][H_I][d_I] */
