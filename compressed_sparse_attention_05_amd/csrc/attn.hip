@@ -692,6 +692,32 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) dequant_group(buf, g);
     };
+    // group g dequantised into registers (stored later by store_group, once
+    // this wave's P.V reads of the buffer are done)
+    auto dequant_regs = [&](int g, uint4 (&h)[4]) {
+        const uint32_t sc = pm_s[g];
+        uint32_t c0 = sc & 0x7fu, c1 = (sc >> 8) & 0x7fu;
+        c0 = c0 < 0x7eu ? c0 : 0x7eu;
+        c1 = c1 < 0x7eu ? c1 : 0x7eu;
+        const half2v s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0 | (c0 << 8), 1.0f, false);
+        const half2v s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1 | (c1 << 8), 1.0f, false);
+        const uint32_t cw[4] = {pm_c[g].x, pm_c[g].y, pm_c[g].z, pm_c[g].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const half2v sv = e < 2 ? s0 : s1;
+            h[e] = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 0) * sv),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 1) * sv),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 2) * sv),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[e], 1.0f, 3) * sv));
+        }
+    };
+    auto store_group = [&](int buf, int g, const uint4 (&h)[4]) {
+        const int key = skey + 16 * g;
+        _Float16* dst = &Kt[buf][key * KROW + 128 * dw + 32 * sp];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(dst + 8 * e) = h[e];
+        if (dw == 0 && sp == 0) kmask[buf][key] = ((pm_ok >> g) & 1u) ? 0.0f : -__builtin_inff();
+    };
     // this D-wave's slice of any tile (main rows, window rows, empty
     // slots), loaded and stored at once; index entries from global memory
     auto load_generic_slice = [&](int tile, int buf) {
@@ -947,11 +973,24 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
             if (it + 2 < n_it && is_main(it + 2)) gather_main(it + 2);
             __syncthreads();
         }
+        // the first two groups of the next tile are dequantised into
+        // registers before P.V, beside the S-waves' products (the VALU and
+        // the matrix cores of a SIMD then overlap), and stored after it
         for (; it < n_it; ++it) {
             const int buf = it & 1;
             const bool next = it + 1 < n_it;
+            uint4 dq0[4], dq1[4];
+            if (next) {
+                dequant_regs(0, dq0);
+                dequant_regs(1, dq1);
+            }
             if (it > 0) pv_tile(buf ^ 1);
-            if (next) dequant_slice(buf ^ 1);
+            if (next) {
+                store_group(buf ^ 1, 0, dq0);
+                store_group(buf ^ 1, 1, dq1);
+                dequant_group(buf ^ 1, 2);
+                dequant_group(buf ^ 1, 3);
+            }
             if (it + 2 < n_it) gather_main(it + 2);
             __syncthreads();
         }
