@@ -278,8 +278,8 @@ int csa2_topk_from_pool(const float* scores, int64_t rows, int64_t ld, const int
 int csa2_pool_topk(const float* block_max, int64_t rows, int64_t n_blocks, int64_t ld_bm, int32_t P_b,
                    int32_t* out_blocks, const float* scores, int64_t ld, int32_t k, int32_t* out_idx,
                    void* stream) {
-    if (rows < 0 || n_blocks < 0 || ld_bm < n_blocks || ld < 0)
-        return fail(CSA2_E_INVALID, "csa2_pool_topk: need rows >= 0, 0 <= n_blocks <= ld_bm, ld >= 0");
+    if (rows < 0 || rows > (int64_t{1} << 30) || n_blocks < 0 || ld_bm < n_blocks || ld < 0)
+        return fail(CSA2_E_INVALID, "csa2_pool_topk: need 0 <= rows <= 2^30, 0 <= n_blocks <= ld_bm, ld >= 0");
     if (k <= 0 || P_b <= 0 || k > P_b)
         return fail(CSA2_E_INVALID, "csa2_pool_topk: need 0 < k <= P_b (the pool holds the top-k only then)");
     if (!csa2::pool_topk_supported(n_blocks, P_b, k))

@@ -252,7 +252,10 @@ __device__ uint32_t count_valid(Get get, int64_t n, uint32_t* wave_tot) {
 //     wave, whose bins it rereads), so no result is published through LDS.
 //     Two histograms alternate: a thread clears its bins of the other one
 //     after the pass's first barrier, when every wave has finished reading
-//     them, so a pass has two barriers.
+//     them, so a pass has two barriers.  When the digit's bin holds at most
+//     kFinMax keys, they are appended to LDS instead and one wave ranks
+//     them (each lane counts the bin's keys above and equal to its own), which
+//     resolves the exact key for a fraction of another pass's cost.
 //  3. Emission: one workgroup scan of (keys above T, keys equal to T) packed
 //     into 16-bit halves gives each thread its output offset and its share
 //     of the ties; it writes its chosen slots in order, so ties go to the
@@ -263,6 +266,8 @@ constexpr int kSelBins = 1 << kSelBits;          // 8 bins per thread
 static_assert(kSelBins == 8 * kThreads, "bin ownership assumes 8 bins per thread");
 static_assert(kSelMax < 65536, "emission packs two counts into 16-bit halves");
 
+constexpr int kFinMax = 64;                      // bin size finished by one wave
+
 struct alignas(16) SelLds {
     uint32_t hist[2][kSelBins];
     uint32_t wave_tot[kWaves];
@@ -271,6 +276,8 @@ struct alignas(16) SelLds {
     uint32_t pass_tot[2][kWaves];
     uint32_t emit_tot[kWaves];
     uint32_t res[4];
+    uint32_t fin[kFinMax];
+    uint32_t fin_cnt;
 };
 
 // Workgroup exclusive scan of one uint32 per thread; returns the prefix and
@@ -342,7 +349,9 @@ __device__ __forceinline__ uint32_t sel_stats(const uint32_t (&kk)[R], SelLds& s
 // subtracted from need, or are never chosen when smaller).  hist[0] must be
 // clear.
 // MAXP: stop after that many passes; *rem_bits (when given) is then the
-// number of low bits still unresolved below the returned prefix.
+// number of low bits still unresolved below the returned prefix.  With
+// MAXP > 1, a bin of at most kFinMax keys left after a pass is resolved
+// exactly by one wave instead of further passes.
 template <int R, bool EARLY = false, int MAXP = 32>
 __device__ __forceinline__ uint32_t sel_passes_from(const uint32_t (&kk)[R], int top, uint64_t known, uint32_t& need,
                                                     SelLds& sh, int* rem_bits = nullptr) {
@@ -370,6 +379,7 @@ __device__ __forceinline__ uint32_t sel_passes_from(const uint32_t (&kk)[R], int
         // thread's bins of it for the next pass
         *reinterpret_cast<uint4*>(&sh.hist[buf ^ 1][hb]) = make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(&sh.hist[buf ^ 1][hb + 4]) = make_uint4(0u, 0u, 0u, 0u);
+        if (tid == 0) sh.fin_cnt = 0u;
         {
             const uint4 lo = *reinterpret_cast<const uint4*>(&hist[hb]);
             const uint4 hi = *reinterpret_cast<const uint4*>(&hist[hb + 4]);
@@ -419,13 +429,44 @@ __device__ __forceinline__ uint32_t sel_passes_from(const uint32_t (&kk)[R], int
         above = rl(above, src);
         known = (known << nb) | digit;
         need -= above;
+        in_bin = rl(in_bin, src);
         if (EARLY && shift > 0) {
-            in_bin = rl(in_bin, src);
             const uint32_t lowest = static_cast<uint32_t>(known) << shift;
             if (in_bin == need && lowest != 0u) {
                 need = 0;
                 return lowest - 1u;
             }
+        }
+        if (MAXP > 1 && shift > 0 && in_bin <= static_cast<uint32_t>(kFinMax)) {
+            // the bin's keys (exactly in_bin of them) to LDS, in any order
+            const uint32_t kp = static_cast<uint32_t>(known);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                if (kk[j] != 0u && (kk[j] >> shift) == kp) sh.fin[atomicAdd(&sh.fin_cnt, 1u)] = kk[j];
+                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            if (wv == 0) {
+                const uint32_t x = lane < static_cast<int>(in_bin) ? sh.fin[lane] : 0u;
+                uint32_t gt = 0, eq = 0;
+                for (int i = 0; i < static_cast<int>(in_bin); ++i) {
+                    const uint32_t y = rl(x, i);
+                    gt += y > x;
+                    eq += y == x;
+                }
+                // the need-th largest: gt < need <= gt + eq (equal keys agree)
+                const bool hit = lane < static_cast<int>(in_bin) && gt < need && gt + eq >= need;
+                const uint64_t hb2 = __ballot(hit);
+                const int at = hb2 ? static_cast<int>(__builtin_ctzll(hb2)) : 0;
+                if (lane == 0) {
+                    sh.res[2] = rl(x, at);
+                    sh.res[3] = need - rl(gt, at);
+                }
+            }
+            __syncthreads();
+            need = sh.res[3];
+            if (rem_bits) *rem_bits = 0;
+            return sh.res[2];
         }
         top = shift - 1;
         buf ^= 1;

@@ -369,88 +369,135 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float* __res
     for (int64_t i = k_eff + threadIdx.x; i < k; i += kThreads) o[i] = -1;
 }
 
-// The Full layer's pool and its top-k in one workgroup per row: the pool is
-// written out (for the Reindex layers) and kept in LDS, and the top-k is then
-// selected among the pool's 8*P_b scores (the identity behind
-// topk_from_pool_kernel).  Direct pool only (n_blocks <= kSelMax); R1 keys
-// per thread for the pool selection, R2 for the top-k.
-template <int R1, int R2>
+// The Full layer's pool and its top-k, two workgroups per row that run side
+// by side (workgroup 2r builds row r's pool, 2r + 1 its top-k).  Direct pool
+// only (n_blocks <= kSelMax), R keys per thread for the block maxima.
+//  * Workgroup 0 selects the P_b best blocks and writes the pool.
+//  * Workgroup 1 does not wait for the pool.  One radix pass over the block
+//    maxima brackets the P_b-th largest maximum in [lo, hi]; every block
+//    whose maximum is >= lo is a candidate.  The candidates hold the pool
+//    (the pool's maxima are all >= the P_b-th largest, hence >= lo), and
+//    the top-k over any set of positions between the pool and the whole
+//    row equals the top-k over the pool (the identity behind
+//    topk_from_pool_kernel), so the top-k is selected among the candidates'
+//    scores.  When more than kCandBlocks blocks reach lo (many equal
+//    maxima), workgroup 1 finishes the exact pool selection itself and uses
+//    the pool's blocks instead.
+constexpr int kCandBlocks = 3072;      // candidate blocks of the top-k workgroup (3 per thread)
+
+template <int R>
 __global__ __launch_bounds__(kThreads) void pool_topk_kernel(const float* __restrict__ bmax, int64_t n_blocks,
                                                              int64_t ld_bm, int P_b, int32_t* __restrict__ pool,
                                                              const float* __restrict__ scores, int64_t ld,
                                                              int k, int32_t* __restrict__ out) {
     __shared__ SelLds sh;
-    __shared__ int32_t pool_s[kPoolMax];
-    const int64_t row = blockIdx.x;
-    uint32_t got_pool = 0, pool_lb = 0, max_key = 0xffffffffu;
-    {
-        const float* bm = bmax + row * ld_bm;
-        int32_t* po = pool + row * static_cast<int64_t>(P_b);
-        const int64_t r0 = static_cast<int64_t>(threadIdx.x) * R1;
-        uint32_t kk[R1];
-        load_run_keys<R1>(bm, r0, n_blocks, kk);
-        auto emit = [&](uint32_t r, int j) {
-            po[r] = static_cast<int32_t>(r0) + j;
-            pool_s[r] = static_cast<int32_t>(r0) + j;
-        };
-        got_pool = select_run<R1>(kk, static_cast<uint32_t>(P_b), sh, emit, &pool_lb, &max_key);
-        const uint32_t got = got_pool;
-        for (int i = static_cast<int>(got) + threadIdx.x; i < P_b; i += kThreads) {
-            po[i] = -1;
-            pool_s[i] = -1;
+    __shared__ int32_t cand_s[kCandBlocks];
+    const int64_t row = blockIdx.x >> 1;
+    const bool topk_wg = (blockIdx.x & 1) != 0;
+    const int tid = threadIdx.x;
+    const int64_t r0 = static_cast<int64_t>(tid) * R;
+    int32_t* po = pool + row * static_cast<int64_t>(P_b);
+    int32_t* o = out + row * static_cast<int64_t>(k);
+    uint32_t kk[R];
+    load_run_keys<R>(bmax + row * ld_bm, r0, n_blocks, kk);
+    uint32_t mn, mx;
+    const uint32_t n_valid = sel_stats<R>(kk, sh, mn, mx);
+    const uint32_t kp = n_valid < static_cast<uint32_t>(P_b) ? n_valid : static_cast<uint32_t>(P_b);
+    const int hb = kSelBins - 8 - 8 * tid;         // this thread's histogram bins
+    uint32_t lb = 0, n_cand = kp;
+    bool exact = !topk_wg;
+    if (topk_wg) {
+        if (kp == 0) {
+            for (int i = tid; i < k; i += kThreads) o[i] = -1;
+            return;
         }
-        // hist[0] for the top-k passes (every read of it ended before the
-        // emission's last barrier)
-        const int hb = kSelBins - 8 - 8 * threadIdx.x;
+        uint32_t need = kp, lo, hi;
+        sel_bracket<R>(kk, mn, mx, need, sh, lo, hi);
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < R; ++j) mine += kk[j] != 0u && kk[j] >= lo;
+        uint32_t n_br;
+        uint32_t at = block_excl_scan(mine, sh.wave_tot, n_br);
+        // every read of hist[0] (the bracket pass) ended before the scan's
+        // barriers: clear this thread's bins for the next selection
+        *reinterpret_cast<uint4*>(&sh.hist[0][hb]) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sh.hist[0][hb + 4]) = make_uint4(0u, 0u, 0u, 0u);
+        if (n_br <= static_cast<uint32_t>(kCandBlocks)) {
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                if (kk[j] != 0u && kk[j] >= lo) cand_s[at++] = static_cast<int32_t>(r0) + j;
+            lb = lo;
+            n_cand = n_br;
+        } else {
+            exact = true;
+            __syncthreads();
+        }
+    }
+    if (exact && kp > 0) {
+        // the exact pool: to HBM from the pool workgroup, to LDS from the
+        // top-k workgroup
+        uint32_t need = kp;
+        const uint32_t T = sel_passes<R, true>(kk, mn, mx, need, sh);
+        sel_emit<R>(kk, T, need, kp, sh, [&](uint32_t r, int j) {
+            const int32_t b = static_cast<int32_t>(r0) + j;
+            if (topk_wg) cand_s[r] = b; else po[r] = b;
+        });
+        lb = need == 0 ? T + 1u : T;
+        // hist[0] was last read before sel_emit's barriers
         *reinterpret_cast<uint4*>(&sh.hist[0][hb]) = make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(&sh.hist[0][hb + 4]) = make_uint4(0u, 0u, 0u, 0u);
     }
+    if (!topk_wg) {
+        for (int i = static_cast<int>(kp) + tid; i < P_b; i += kThreads) po[i] = -1;
+        return;
+    }
     __syncthreads();
     const float* s = scores + row * ld;
-    int32_t* o = out + row * static_cast<int64_t>(k);
     const bool aligned = (reinterpret_cast<uintptr_t>(s) & 31u) == 0;
-    constexpr int NB = R2 / 8;
-    const int b0 = threadIdx.x * NB;
+    constexpr int NB = kCandBlocks / kThreads;
+    constexpr int R2 = 8 * NB;
+    const int b0 = tid * NB;
     int32_t blk[NB];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) blk[q] = (b0 + q < P_b) ? pool_s[b0 + q] : -1;
-    uint32_t kk[R2];
+    for (int q = 0; q < NB; ++q) blk[q] = (b0 + q < static_cast<int>(n_cand)) ? cand_s[b0 + q] : -1;
+    uint32_t k2[R2];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
         const int64_t p0 = static_cast<int64_t>(blk[q]) * 8;
         if (blk[q] >= 0 && aligned && p0 + 8 <= ld) {
             const float4 v0 = *reinterpret_cast<const float4*>(s + p0);
             const float4 v1 = *reinterpret_cast<const float4*>(s + p0 + 4);
-            kk[8 * q + 0] = key_of(v0.x); kk[8 * q + 1] = key_of(v0.y);
-            kk[8 * q + 2] = key_of(v0.z); kk[8 * q + 3] = key_of(v0.w);
-            kk[8 * q + 4] = key_of(v1.x); kk[8 * q + 5] = key_of(v1.y);
-            kk[8 * q + 6] = key_of(v1.z); kk[8 * q + 7] = key_of(v1.w);
+            k2[8 * q + 0] = key_of(v0.x); k2[8 * q + 1] = key_of(v0.y);
+            k2[8 * q + 2] = key_of(v0.z); k2[8 * q + 3] = key_of(v0.w);
+            k2[8 * q + 4] = key_of(v1.x); k2[8 * q + 5] = key_of(v1.y);
+            k2[8 * q + 6] = key_of(v1.z); k2[8 * q + 7] = key_of(v1.w);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                kk[8 * q + e] = (blk[q] >= 0 && p0 + e < ld) ? key_of(s[p0 + e]) : 0u;
+                k2[8 * q + e] = (blk[q] >= 0 && p0 + e < ld) ? key_of(s[p0 + e]) : 0u;
         }
     }
-    // Every chosen block's maximum is >= pool_lb, so with a full pool of P_b
-    // >= k blocks at least k pool scores are >= pool_lb and the k-th best
-    // score is too: scores below it cannot be chosen and leave the
-    // selection as empty slots, which keeps them out of its histograms.
-    // With a full pool those scores also lie in [pool_lb, max_key] (no score
-    // exceeds the largest block maximum) and at least k of them are
-    // nonempty, so the selection needs no count or range pass of its own.
-    auto out_pos = [&](uint32_t r, int j) { o[r] = blk[j >> 3] * 8 + (j & 7); };
-    uint32_t got;
-    if (got_pool == static_cast<uint32_t>(P_b) && pool_lb != 0u) {
+    // With kp == P_b >= k, at least k candidate blocks have a maximum >= lb,
+    // so at least k scores are >= lb and the k-th best is too: scores below
+    // lb cannot be chosen and leave the selection as empty slots.  The rest
+    // lie in [lb, mx] (no score exceeds the largest block maximum) and at
+    // least k of them are nonempty, so the selection needs no count or range
+    // pass of its own.  A short pool (fewer than P_b nonempty blocks) takes
+    // the count and range of its scores first.
+    uint32_t k_eff = static_cast<uint32_t>(k), key_lo = lb, key_hi = mx;
+    if (kp == static_cast<uint32_t>(P_b) && lb != 0u) {
 #pragma unroll
-        for (int e = 0; e < R2; ++e) kk[e] = kk[e] >= pool_lb ? kk[e] : 0u;
-        uint32_t need = static_cast<uint32_t>(k);
-        const uint32_t T = sel_passes<R2, true>(kk, pool_lb, max_key, need, sh);
-        sel_emit<R2>(kk, T, need, static_cast<uint32_t>(k), sh, out_pos);
-        got = static_cast<uint32_t>(k);
+        for (int e = 0; e < R2; ++e) k2[e] = k2[e] >= lb ? k2[e] : 0u;
     } else {
-        got = select_run<R2>(kk, static_cast<uint32_t>(k), sh, out_pos);
+        const uint32_t n2 = sel_stats<R2>(k2, sh, key_lo, key_hi);
+        k_eff = n2 < k_eff ? n2 : k_eff;
     }
-    for (int i = static_cast<int>(got) + threadIdx.x; i < k; i += kThreads) o[i] = -1;
+    if (k_eff > 0) {
+        uint32_t need = k_eff;
+        const uint32_t T = sel_passes<R2, true>(k2, key_lo, key_hi, need, sh);
+        sel_emit<R2>(k2, T, need, k_eff, sh, [&](uint32_t r, int j) { o[r] = blk[j >> 3] * 8 + (j & 7); });
+    }
+    for (int i = static_cast<int>(k_eff) + tid; i < k; i += kThreads) o[i] = -1;
 }
 
 }  // namespace
@@ -462,13 +509,13 @@ bool pool_topk_supported(int64_t n_blocks, int P_b, int k) {
 hipError_t launch_pool_topk(const float* bmax, int64_t rows, int64_t n_blocks, int64_t ld_bm, int P_b,
                             int32_t* pool, const float* scores, int64_t ld, int k, int32_t* out, hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>(rows));
-    // the pool's 8*P_b <= 16,384 scores always fit 16 per thread (P_b <= 2,048)
-    static_assert(8 * kPoolMax <= 16 * kThreads, "pool scores: 16 per thread");
+    const dim3 grid(static_cast<unsigned>(2 * rows));
+    // the exact pool (P_b <= 2,048 blocks) always fits the candidate list
+    static_assert(kPoolMax <= kCandBlocks && kCandBlocks % kThreads == 0, "candidate blocks");
     if (n_blocks <= 16 * kThreads)
-        pool_topk_kernel<16, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+        pool_topk_kernel<16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
     else
-        pool_topk_kernel<32, 16><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
+        pool_topk_kernel<32><<<grid, kThreads, 0, st>>>(bmax, n_blocks, ld_bm, P_b, pool, scores, ld, k, out);
     return hipGetLastError();
 }
 

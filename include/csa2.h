@@ -248,11 +248,14 @@ int csa2_topk_from_pool(const float *scores, int64_t rows, int64_t ld, const int
  * in one launch ([KVC] section 3: the first Full layer scores every
  * position and builds the pool in the same pass).  Same outputs, bit for
  * bit, as the two calls: out_blocks [rows][P_b] as csa2_build_candidate_pool
- * writes it, out_idx [rows][k] as csa2_topk_from_pool writes it.  The pool
- * stays on chip between the two selections, so one workgroup per row does
- * both.  Requires 0 < k <= P_b <= 2048 and n_blocks <= 32,768 (the pool
- * selected directly, without super-blocks); other sizes return
- * CSA2_E_UNSUPPORTED and the two calls remain.
+ * writes it, out_idx [rows][k] as csa2_topk_from_pool writes it.  Two
+ * workgroups per row run side by side: one selects and writes the pool, the
+ * other selects the top-k among the scores of every block whose maximum
+ * reaches a one-pass lower bound of the pool threshold (a superset of the
+ * pool, so the same top-k).  Requires 0 < k <= P_b <= 2048,
+ * n_blocks <= 32,768 (the pool selected directly, without super-blocks)
+ * and rows <= 2^30; other sizes return CSA2_E_UNSUPPORTED (CSA2_E_INVALID
+ * for rows) and the two calls remain.
  * block_max [rows][ld_bm]; scores [rows][ld] (position order, -inf where
  * invisible).  No workspace.
  * ------------------------------------------------------------------------ */

@@ -253,7 +253,7 @@ def test_pool_through_superblocks(K):
 
 @pytest.mark.parametrize("n", [70000, 262144])
 def test_pool_topk_fused_equals_two_calls(K, n):
-    # csa2_pool_topk = pool then the Full top-k inside it, in one launch:
+    # csa2_pool_topk = pool and the Full top-k inside it, in one launch:
     # 70,000 positions (16 block maxima per thread) and 262,144 (32 per
     # thread, the largest row the fused path takes)
     rng = np.random.default_rng(12)
@@ -272,6 +272,32 @@ def test_pool_topk_fused_equals_two_calls(K, n):
             assert np.array_equal(pool[r], oracle.candidate_pool(bm[r], P_b)), (r, k)
             assert np.array_equal(idx[r], oracle.topk(v[r], k)), (r, k)
 
+
+
+@pytest.mark.parametrize("n", [70000, 262144])
+def test_pool_topk_many_tied_block_maxima(K, n):
+    # The top-k workgroup of csa2_pool_topk takes every block whose maximum
+    # reaches the lower edge of the radix bin holding the P_b-th largest
+    # maximum; with more than 3,072 such blocks it selects the exact pool
+    # itself.  Rows 0-2 reach that (all maxima equal, a few values tied by
+    # thousands, 2,047 distinct maxima above a plateau); row 3 stays on the
+    # bracket with somewhat more than P_b blocks.
+    rng = np.random.default_rng(13)
+    P_b = 2048
+    v = np.abs(rng.standard_normal((4, n))).astype(np.float32)
+    v[0] = 1.5
+    v[1] = np.round(v[1] * 2)
+    v[2] = 0.25
+    v[2, 64:64 + 8 * 2047:8] = 5 + np.arange(2047, dtype=np.float32)
+    v[3] = np.round(v[3] * 64) / 64 + 3
+    nb = (n + 7) // 8
+    bm = np.stack([oracle.block_max(v[r], n, nb) for r in range(4)])
+    for k in (1, 2047, 2048):
+        pool, idx = K.csa2_pool_topk(dev(torch.from_numpy(bm)), dev(torch.from_numpy(v)), P_b, k)
+        pool, idx = pool.cpu().numpy(), idx.cpu().numpy()
+        for r in range(4):
+            assert np.array_equal(pool[r], oracle.candidate_pool(bm[r], P_b)), (r, k)
+            assert np.array_equal(idx[r], oracle.topk(v[r], k)), (r, k)
 
 def test_topk_small_rows_exhaustive(K):
     rng = np.random.default_rng(8)
