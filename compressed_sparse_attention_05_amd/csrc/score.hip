@@ -19,7 +19,10 @@
 //    feeds two fmas and the bf16 -> f32 widening costs one op per channel.
 //  * The query, transposed to [d_I][H_I] float32, sits in LDS and is read
 //    with same-address (broadcast) 16-byte reads; LDS completions are in
-//    order, so reads for the next channel overlap the current fmas.
+//    order, so reads for the next channel overlap the current fmas.  Each
+//    wave scores one unit of 128 positions.  The workgroup's threads load
+//    the query, issue their first key loads, and only then stage the query
+//    and meet the barrier, which waits for LDS and not for the key loads.
 //  * The block max over 8 positions (candidate-pool input, notes section 3)
 //    is fused: 8 consecutive lanes own one block.
 #include <type_traits>
@@ -59,7 +62,7 @@ struct ScoreArgs {
     int64_t gx_scan;
 };
 
-template <int HI, int DI, bool KBF16, bool WR>
+template <int HI, int DI, bool KBF16, bool WR, bool FULL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(const void* __restrict__ q_all,
                                                          const float* __restrict__ w_all,
                                                          const uint8_t* __restrict__ k_all,
@@ -99,23 +102,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         return;
     }
 
-    // query -> LDS, transposed to [c][h], widened to float32
-    for (int i = t; i < HI * DI; i += kThreads) {
-        const int h = i / DI, c = i % DI;
-        float v;
-        if (a.q_bf16)
-            v = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q_all)[row * HI * DI + i]) << 16);
-        else
-            v = static_cast<const float*>(q_all)[row * HI * DI + i];
-        qs[c * HI + h] = v;
+    // This thread's share of the query: channel qc, heads qh .. qh+QH-1,
+    // which is one contiguous run of the [c][h] layout in LDS.  Full scan
+    // (FULL, no pool): loaded raw first and staged only after the wave's
+    // first key loads are issued, so the query and key latencies overlap (the
+    // barrier waits for LDS only, not for the key loads).  Pool scan: staged
+    // first, before the pool lookup.
+    constexpr int QH = HI < 4 ? HI : 4;           // heads per thread
+    constexpr int QT = DI * HI / QH;              // threads that stage the query
+    static_assert(QT <= kThreads, "query staging fits the workgroup");
+    const bool q_thr = t < QT;
+    const int qc = t / (HI / QH), qh = (t % (HI / QH)) * QH;
+    uint32_t qraw[QH];                            // bf16 held unshifted until staged
+    if (q_thr) {
+        const int64_t q0 = row * HI * DI + static_cast<int64_t>(qh) * DI + qc;
+        if (a.q_bf16) {
+#pragma unroll
+            for (int j = 0; j < QH; ++j) qraw[j] = static_cast<const uint16_t*>(q_all)[q0 + j * DI];
+        } else {
+#pragma unroll
+            for (int j = 0; j < QH; ++j) qraw[j] = static_cast<const uint32_t*>(q_all)[q0 + j * DI];
+        }
     }
+    auto stage_q = [&]() {
+        if (q_thr) {
+            float v[QH];
+#pragma unroll
+            for (int j = 0; j < QH; ++j) v[j] = __uint_as_float(a.q_bf16 ? qraw[j] << 16 : qraw[j]);
+            float* dst = qs + qc * HI + qh;
+            if constexpr (QH == 4)
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            else
+#pragma unroll
+                for (int j = 0; j < QH; ++j) dst[j] = v[j];
+        }
+        __syncthreads();
+    };
+    if constexpr (!FULL) stage_q();
     float wh[HI];
 #pragma unroll
     for (int h = 0; h < HI; ++h) wh[h] = w_all[row * HI + h];
-    __syncthreads();
 
     const uint8_t* kb = k_all + b * a.cap * ROWB;        // cap is a multiple of 64
-    const int32_t* pool = a.pool ? a.pool + row * a.P_b : nullptr;
+    const int32_t* pool = FULL ? nullptr : a.pool + row * a.P_b;
     int64_t vis = a.ctx_len[b];
     if (a.q_pos) {
         const int64_t v2 = (a.q_pos[row] + 1) / a.m;
@@ -134,10 +163,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         return pos < vis ? pos : -1;
     };
 
-    const int64_t u0 = static_cast<int64_t>(blockIdx.x) * a.units_per_wg;
-    int64_t u1 = u0 + a.units_per_wg;
-    if (u1 > a.units_per_row) u1 = a.units_per_row;
-
     // position of the entry this launch writes for sequence b (-1: none);
     // the unit holding it reads that row's key from knew (16-byte chunk
     // stride) instead of the tiled cache (1 KiB chunk stride)
@@ -148,52 +173,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     const uint8_t* knew_row = WR ? a.knew + b * ROWB : nullptr;
 
-    for (int64_t u = u0 + wv; u < u1; u += kWaves) {
-        int64_t slot[2], pos[2];
+    // one unit per wave (units_per_wg == kWaves); a wave past the row's last
+    // unit stages its query share and meets the barrier, then stops
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * a.units_per_wg + wv;
+    const bool has_unit = u < a.units_per_row;
+    int64_t slot[2], pos[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            slot[p] = u * kUnit + p * 64 + lane;
-            pos[p] = pos_of(slot[p]);
-        }
-        const bool has_new = WR && np >= 0 && __ballot(pos[0] == np || pos[1] == np) != 0;   // wave-uniform
-        auto unit = [&](auto newrow) {
-        constexpr bool NR = decltype(newrow)::value;
-        const uint8_t* base[2];
-        int cstride[2];
+    for (int p = 0; p < 2; ++p) {
+        slot[p] = u * kUnit + p * 64 + lane;
+        pos[p] = pos_of(slot[p]);        // -1 past the row's slots
+    }
+    const bool has_new = WR && np >= 0 && __ballot(pos[0] == np || pos[1] == np) != 0;   // wave-uniform
+    // Stream the row chunks in groups of G; the group loop is not unrolled
+    // so the compiler cannot hoist every load and query read at once.  Every
+    // load is unconditional: invisible positions read row 0 of the sequence
+    // and are masked when the score is written, and the last group's "next"
+    // load repeats the last group, so no load sits in a lane-divergent
+    // branch.  In the Full scan the first group goes out before the query is
+    // staged (with the tiled addressing; the unit holding the new entry
+    // reloads it with its own).
+    const uint8_t* base[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int64_t pp = pos[p] < 0 ? 0 : pos[p];
-            base[p] = kb + ((pp >> 6) * NCH * 64 + (pp & 63)) * 16;
-            cstride[p] = 1024;
-            if (NR && pos[p] == np) { base[p] = knew_row; cstride[p] = 16; }
-        }
-        // Stream the row chunks in groups of G (registers hold the current
-        // group and the next one in flight); the group loop is not unrolled
-        // so the compiler cannot hoist every load and query read at once.
-        // Every load is unconditional: invisible positions read row 0 of the
-        // sequence and are masked when the score is written, and the last
-        // group's "next" load repeats the last group, so no load sits in a
-        // lane-divergent branch.
-        constexpr int NG = NCH / G;
-        uint4 cur[2][G];
+    for (int p = 0; p < 2; ++p) {
+        const int64_t pp = pos[p] < 0 ? 0 : pos[p];
+        base[p] = kb + ((pp >> 6) * NCH * 64 + (pp & 63)) * 16;
+    }
+    uint4 cur[2][G];
+    if constexpr (FULL) {
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
-            for (int p = 0; p < 2; ++p) cur[p][j] = *reinterpret_cast<const uint4*>(base[p] + j * (NR ? cstride[p] : 1024));
+            for (int p = 0; p < 2; ++p) cur[p][j] = *reinterpret_cast<const uint4*>(base[p] + j * 1024);
+        stage_q();
+    }
+    if (!has_unit) return;
+
+    auto unit = [&](auto newrow) {
+        constexpr bool NR = decltype(newrow)::value;
+        int cstride[2] = {1024, 1024};
+        constexpr int NG = NCH / G;
+        auto load_group = [&](uint4 (&dst)[2][G], int g) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    dst[p][j] = *reinterpret_cast<const uint4*>(base[p] + (g * G + j) * (NR ? cstride[p] : 1024));
+        };
+        if (NR) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                if (pos[p] == np) { base[p] = knew_row; cstride[p] = 16; }
+        }
+        if (FULL && NR) load_group(cur, 0);
         float acc[2][HI];
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
             for (int h = 0; h < HI; ++h) acc[p][h] = 0.0f;
-#pragma unroll 1
-        for (int g = 0; g < NG; ++g) {
-            const int gn = g + 1 < NG ? g + 1 : g;
-            uint4 nxt[2][G];
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-#pragma unroll
-                for (int p = 0; p < 2; ++p)
-                    nxt[p][j] = *reinterpret_cast<const uint4*>(base[p] + (gn * G + j) * (NR ? cstride[p] : 1024));
+        auto fma_group = [&](const uint4 (&src)[2][G], int g) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const int c = g * G + j;
@@ -201,15 +238,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     if (KBF16) {
-                        const uint32_t wd[4] = {cur[p][j].x, cur[p][j].y, cur[p][j].z, cur[p][j].w};
+                        const uint32_t wd[4] = {src[p][j].x, src[p][j].y, src[p][j].z, src[p][j].w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             kv[p][2 * e] = __uint_as_float(wd[e] << 16);
                             kv[p][2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
                         }
                     } else {
-                        kv[p][0] = __uint_as_float(cur[p][j].x); kv[p][1] = __uint_as_float(cur[p][j].y);
-                        kv[p][2] = __uint_as_float(cur[p][j].z); kv[p][3] = __uint_as_float(cur[p][j].w);
+                        kv[p][0] = __uint_as_float(src[p][j].x); kv[p][1] = __uint_as_float(src[p][j].y);
+                        kv[p][2] = __uint_as_float(src[p][j].z); kv[p][3] = __uint_as_float(src[p][j].w);
                     }
                 }
 #pragma unroll
@@ -233,10 +270,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                     }
                 }
             }
+        };
+        if constexpr (FULL) {
+            // One group's fmas run while the next group's loads are in
+            // flight.  The scheduling barriers keep those loads ahead of the
+            // fmas and the cur = nxt copy behind them: left alone, the
+            // scheduler moves each chunk's copy up to where the matching chunk
+            // of cur is consumed (or folds the pair into load-then-wait), and
+            // the wave then waits for a load it has just issued.
+#pragma unroll 1
+            for (int g = 0; g < NG; ++g) {
+                const int gn = g + 1 < NG ? g + 1 : g;
+                uint4 nxt[2][G];
+                load_group(nxt, gn);
+                __builtin_amdgcn_sched_barrier(0);
+                fma_group(cur, g);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < G; ++j)
+                for (int j = 0; j < G; ++j)
 #pragma unroll
-                for (int p = 0; p < 2; ++p) cur[p][j] = nxt[p][j];
+                    for (int p = 0; p < 2; ++p) cur[p][j] = nxt[p][j];
+            }
+        } else {
+            // Pool scan (rows gathered through the pool): each group's loads
+            // all go out, then its fmas consume them, with the other waves of
+            // the CU hiding the latency; a prefetched next group measured
+            // slower here.
+#pragma unroll 1
+            for (int g = 0; g < NG; ++g) {
+                load_group(cur, g);
+                if constexpr (!NR) __builtin_amdgcn_sched_barrier(0);   // (spills in the new-entry unit)
+                fma_group(cur, g);
+            }
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -255,10 +320,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 if ((lane & 7) == 0 && blk < a.ld_bm) block_max[row * a.ld_bm + blk] = mx;
             }
         }
-        };
-        if (has_new) unit(std::true_type{});
-        else unit(std::false_type{});
-    }
+    };
+    if (has_new) unit(std::true_type{});
+    else unit(std::false_type{});
 }
 
 template <int HI, int DI, bool KBF16>
@@ -288,12 +352,15 @@ hipError_t launch_typed(const ScoreLaunch& p, hipStream_t st) {
     // the write's code paths are a separate instantiation, so a scan without
     // a write keeps its own register allocation
     const dim3 grid(static_cast<unsigned>(gx_all), static_cast<unsigned>(rows));
-    if (p.knew)
-        score_kernel<HI, DI, KBF16, true><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, static_cast<const uint8_t*>(p.k_idx),
-                                                                     p.scores, p.block_max, a);
+    const uint8_t* kx = static_cast<const uint8_t*>(p.k_idx);
+    if (p.knew && !p.pool)
+        score_kernel<HI, DI, KBF16, true, true><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, kx, p.scores, p.block_max, a);
+    else if (p.knew)
+        score_kernel<HI, DI, KBF16, true, false><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, kx, p.scores, p.block_max, a);
+    else if (!p.pool)
+        score_kernel<HI, DI, KBF16, false, true><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, kx, p.scores, p.block_max, a);
     else
-        score_kernel<HI, DI, KBF16, false><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, static_cast<const uint8_t*>(p.k_idx),
-                                                                      p.scores, p.block_max, a);
+        score_kernel<HI, DI, KBF16, false, false><<<grid, kThreads, 0, st>>>(p.q_idx, p.w, kx, p.scores, p.block_max, a);
     return hipGetLastError();
 }
 

@@ -148,7 +148,7 @@ int csa2_kv_write_project(const void *x, int x_dtype, int64_t n_rows, int32_t D,
 typedef struct csa2_score_args {
     const void *q_idx;  int32_t q_dtype;  /* [B][Tq][H_I][d_I] */
     const float *w;                       /* [B][Tq][H_I] */
-    const void *k_idx;  int32_t k_dtype;  /* B*cap rows of d_I, tiled layout */
+    const void *k_idx;  int32_t k_dtype;  /* B*cap rows of d_I, tiled layout, 16-byte aligned */
     int64_t B, Tq, cap;
     int32_t H_I, d_I;
     const int32_t *ctx_len;               /* [B] */
