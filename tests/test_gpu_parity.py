@@ -240,15 +240,23 @@ def test_topk_from_pool_equals_full_topk(K):
             assert np.array_equal(got[r], oracle.topk(v[r], k)), (r, k)
 
 
-def test_pool_through_superblocks(K):
+@pytest.mark.parametrize("nb,ld", [(131075, 131075), (131069, 131069), (100003, 100003),
+                                   (131072, 131072), (131069, 131072)])
+def test_pool_through_superblocks(K, nb, ld):
+    # > 32,768 blocks.  131,075 takes 32 super-blocks per thread.  The others
+    # take 16: with odd strides (131,069 and 100,003 per row) rows are not
+    # 16-byte aligned and each thread reads its own run; a stride that is a
+    # multiple of 4 reads the rows coalesced, 131,069 of 131,072 with a
+    # partial last float4
     rng = np.random.default_rng(11)
-    rows, nb, P_b = 3, 131075, 2048             # > 32768 blocks, ragged tail
-    bm = np.abs(rng.standard_normal((rows, nb))).astype(np.float32) * 20
-    bm[1] = np.round(bm[1] / 4)                 # heavy ties
-    bm[2, 100000:] = -np.inf
-    got = K.csa2_build_candidate_pool(dev(torch.from_numpy(bm)), P_b).cpu().numpy()
+    rows, P_b = 3, 2048
+    full = np.abs(rng.standard_normal((rows, ld))).astype(np.float32) * 20
+    full[1] = np.round(full[1] / 4)             # heavy ties
+    full[2, nb - 31075:] = -np.inf
+    full[:, nb:] = 1e30                         # past n_blocks: must be ignored
+    got = K.csa2_build_candidate_pool(dev(torch.from_numpy(full)), P_b, n_blocks=nb).cpu().numpy()
     for r in range(rows):
-        assert np.array_equal(got[r], oracle.candidate_pool(bm[r], P_b)), r
+        assert np.array_equal(got[r], oracle.candidate_pool(full[r, :nb], P_b)), r
 
 
 @pytest.mark.parametrize("n", [70000, 262144])
