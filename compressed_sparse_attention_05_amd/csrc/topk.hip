@@ -433,8 +433,8 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float* __res
 // The Full layer's pool and its top-k, two workgroups per row that run side
 // by side (workgroup 2r builds row r's pool, 2r + 1 its top-k).  Direct pool
 // only (n_blocks <= kSelMax), R keys per thread for the block maxima.
-//  * Workgroup 0 selects the P_b best blocks and writes the pool.
-//  * Workgroup 1 does not wait for the pool.  One radix pass over the block
+//  * The pool workgroup selects the P_b best blocks and writes the pool.
+//  * The top-k workgroup does not wait for it.  One radix pass over the block
 //    maxima brackets the P_b-th largest maximum in [lo, hi]; every block
 //    whose maximum is >= lo is a candidate.  The candidates hold the pool
 //    (the pool's maxima are all >= the P_b-th largest, hence >= lo), and
@@ -442,8 +442,8 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float* __res
 //    row equals the top-k over the pool (the identity behind
 //    topk_from_pool_kernel), so the top-k is selected among the candidates'
 //    scores.  When more than kCandBlocks blocks reach lo (many equal
-//    maxima), workgroup 1 finishes the exact pool selection itself and uses
-//    the pool's blocks instead.
+//    maxima), the top-k workgroup finishes the exact pool selection itself
+//    and uses the pool's blocks instead.
 constexpr int kCandBlocks = 3072;      // candidate blocks of the top-k workgroup (3 per thread)
 
 template <int R>
