@@ -284,7 +284,7 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
     // candidate slot of the row)
     int32_t lim[2][2];
     float thf[2][2];
-    float* sbase[2][2];
+    uint32_t soff[2][2];                 // SAMPLE: byte offset of this lane's sample slot 0 in the wave's buffer
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -296,15 +296,19 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
             if (v > n_cols) v = n_cols;
             lim[mt][e] = static_cast<int32_t>(v - (lane & 31));
             thf[mt][e] = SAMPLE ? 0.0f : thr_float(thr[tc - t0]);
-            sbase[mt][e] = SAMPLE ? samp + (tc - t0) * ld_s + (lane & 31) : nullptr;
+            // rows past the chunk get an offset past the buffer, so their
+            // stores are dropped
+            soff[mt][e] = ok ? static_cast<uint32_t>(((t - qb) * ld_s + (lane & 31)) * 4) : 0x80000000u;
         }
-    // the wave's 8 candidate rows as one buffer (byte range below 2^31,
-    // which the launch checks; rows past the chunk are outside the range)
+    // the wave's 8 candidate rows (sample rows: SAMPLE) as one buffer (byte
+    // range below 2^31, which the launch checks; rows past the chunk are
+    // outside the range)
     int64_t rows_here = t1 - qb;
     rows_here = rows_here < 0 ? 0 : (rows_here > 8 ? 8 : rows_here);
     const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
-        SAMPLE ? static_cast<void*>(samp) : static_cast<void*>(cand + (qb < t1 ? qb - t0 : 0) * g.cand_ld),
-        static_cast<short>(0), SAMPLE ? 0 : static_cast<int>(rows_here * g.cand_ld * 8), 0x00020000);
+        SAMPLE ? static_cast<void*>(samp + (qb < t1 ? qb - t0 : 0) * ld_s)
+               : static_cast<void*>(cand + (qb < t1 ? qb - t0 : 0) * g.cand_ld),
+        static_cast<short>(0), static_cast<int>(rows_here * (SAMPLE ? ld_s * 4 : g.cand_ld * 8)), 0x00020000);
     // uniform slot of the next candidate of wave row q (4mt + query) in the
     // wave's buffer: q * cand_ld + the workgroup's first slot + the count so far
     const uint32_t slot0 = static_cast<uint32_t>(bx * (kSub * g.blocks));
@@ -395,8 +399,15 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(PfArgs a, int64_t t0, i
                 const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                 const bool vis_ok = !VIS || jb32 < lim[mt][e];
                 if (SAMPLE) {
+                    // unconditional: a slot past the row's groups is past the
+                    // buffer (bit 31), and the hardware drops the store.  (A
+                    // guarded store made the compiler wait for every store
+                    // before the next tile's staging.)
                     const int64_t gi = jb / kGroup;
-                    if (gi * kSub < ld_s) sbase[mt][e][gi * kSub] = vis_ok ? v : -__builtin_inff();
+                    const uint32_t off = (soff[mt][e] + static_cast<uint32_t>(gi * kSub * 4)) |
+                                         (gi * kSub < ld_s ? 0u : 0x80000000u);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vis_ok ? v : -__builtin_inff()), crsrc,
+                                                          static_cast<int>(off), 0, 0);
                 } else {
                     // (s~ bits, position) of taken keys go straight to the
                     // row's next slots, in position order: the lower half of
@@ -961,6 +972,7 @@ hipError_t launch_prefill_topk(const PrefillLaunch& L, void* ws, hipStream_t st)
         const int64_t cols = prefill_cols(t1, L.ctx_len, L.q_pos0, L.m);   // widest row of the chunk
         const int qblocks = static_cast<int>(cdiv(rows, kQB));
         if (cols > kCandCap) {
+            if (8 * 4 * w.ld_s > 0x7fffffffLL) return hipErrorInvalidValue;   // a wave's sample rows as one buffer
             Geo gs = make_geo(cdiv(cols, kGroup), qblocks, 16, 1 << 20, n_cu);
             score_mfma_kernel<true><<<grid_of(gs), 512, 0, st>>>(a, t0, t1, cols, gs, w.samp, w.ld_s, nullptr,
                                                                   nullptr, nullptr);
