@@ -190,6 +190,27 @@ def _topk_check(K, vals, k, pool=None):
         assert np.array_equal(got[r], want), r
 
 
+
+@pytest.mark.parametrize("n", [16384, 32768])
+def test_topk_threshold_in_a_small_tied_bin(K, n):
+    # The k-th key falls in a radix bin that holds only a cluster of 40 keys
+    # near 50 (no other key lies in [40, 60)): the selection finishes such a
+    # bin in one wave.  Rows 0-1: cluster values 2^-16 apart, some repeated;
+    # rows 2-3: steps of 2^-20, which round to four float32 values (the ulp
+    # at 50 is 2^-18), so the k-th key is tied many times over.
+    rng = np.random.default_rng(21)
+    rows = 4
+    v = np.empty((rows, n), np.float32)
+    for r in range(rows):
+        hi = rng.uniform(60, 100, 2000)
+        lo = rng.uniform(0, 40, n - 2040)
+        steps = np.sort(rng.integers(0, 30 if r < 2 else 12, 40))
+        cluster = 50.0 + steps * 2.0 ** (-16 if r < 2 else -20)
+        row = np.concatenate([hi, cluster, lo]).astype(np.float32)
+        v[r] = row[rng.permutation(n)]
+    for k in (2001, 2020, 2039, 2040):
+        _topk_check(K, v, k)
+
 def test_topk_random_and_ties(K):
     rng = np.random.default_rng(7)
     v = rng.standard_normal((6, 20000)).astype(np.float32)
