@@ -102,9 +102,11 @@ def test_prefill_topk_full_chunk_sampled(K):
 # one 32-key block per 512 keys is scored first, the row's candidates are
 # the keys at or above a sample quantile, and the final pass checks that
 # they cover the band around the k-th score.
-@pytest.mark.parametrize("k", [512, 2048])
-def test_prefill_topk_sampled_threshold(K, k):
-    T, cap, m = 64, 40960, 2
+@pytest.mark.parametrize("k,T", [(512, 64), (2048, 64), (2048, 13)])
+def test_prefill_topk_sampled_threshold(K, k, T):
+    # T = 13: the last block of 8 query rows has 3 rows past the chunk,
+    # whose sample stores must be dropped
+    cap, m = 40960, 2
     q_pos0 = 2 * cap - 2 * T          # vis(t) runs from cap - T to cap
     q, w, kc = _inputs(2004, T, cap)
     print(f"prefill topk sampled T={T} cap={cap} k={k}", flush=True)
