@@ -1005,24 +1005,24 @@ __global__ __launch_bounds__(512) void attn_ws_kernel(AttnArgs a) {
                 __syncthreads();
             }
         } else {
-        // the next tile is dequantised inside P.V, group by group (the
-        // first iteration has no P.V, the last no next tile: both peeled)
-        if (it == 0 && n_it > 1) {
-            dequant_slice(1);
-            if (n_it > 2) gather_main(2);
-            __syncthreads();
-            it = 1;
-        }
-        for (; it + 1 < n_it; ++it) {
-            const int buf = it & 1;
-            pv_tile(buf ^ 1, true);
-            if (it + 2 < n_it) gather_main(it + 2);
-            __syncthreads();
-        }
-        if (it < n_it) {
-            if (it > 0) pv_tile((it & 1) ^ 1, false);
-            __syncthreads();
-        }
+            // the next tile is dequantised inside P.V, group by group (the
+            // first iteration has no P.V, the last no next tile: both peeled)
+            if (it == 0 && n_it > 1) {
+                dequant_slice(1);
+                if (n_it > 2) gather_main(2);
+                __syncthreads();
+                it = 1;
+            }
+            for (; it + 1 < n_it; ++it) {
+                const int buf = it & 1;
+                pv_tile(buf ^ 1, true);
+                if (it + 2 < n_it) gather_main(it + 2);
+                __syncthreads();
+            }
+            if (it < n_it) {
+                if (it > 0) pv_tile((it & 1) ^ 1, false);
+                __syncthreads();
+            }
         }
         if (n_it > 0) pv_tile((n_it - 1) & 1, false);
     }
