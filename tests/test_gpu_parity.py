@@ -446,13 +446,16 @@ def test_attention_prefill_window(K):
         assert err < ATOL
 
 
-@pytest.mark.parametrize("T", [520, 1024])
-def test_attention_prefill_long_split_sampled(K, T):
+@pytest.mark.parametrize("T,k", [(520, 2048), (1024, 2048), (1024, 2000)])
+def test_attention_prefill_long_split_sampled(K, T, k):
     """Many query units on the warp-specialised kernel: 520 units take two
     key splits per query; 1,024 units take one, so each workgroup walks all
     34 key tiles of its query (index list restaged in windows) and writes
-    the output directly.  Sampled queries vs the oracle."""
-    N, D, H, k, W = 40000, 512, 64, 2048, 128
+    the output directly.  These long splits dequantise the next tile inside
+    P.V; with k = 2,000 the split starts with three generic tiles, the first
+    of them 16 main entries and 48 window rows.  Sampled queries vs the
+    oracle."""
+    N, D, H, W = 40000, 512, 64, 128
     seed = 302
     kv = ci.gaussian(seed, ci.TID_KV, (N, D), dtype=torch.float32)
     codes, scales = oracle.mxfp4_encode(kv)
