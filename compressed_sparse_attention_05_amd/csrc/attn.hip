@@ -1205,7 +1205,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const _Float16* __restric
 struct SplitPlan { int splits, tiles_per_split, n_tiles; };
 
 // splits of at least this many tiles run attn_ws_kernel with the next tile's
-// dequantisation inside P.V (measured: prefill, one split of 34 tiles, 4.5%
+// dequantisation inside P.V (measured: prefill, one split of 34 tiles, 3.5-4.5%
 // faster; 9-tile splits unchanged; 3-tile splits 0.9% slower)
 constexpr int kIlvTiles = 16;
 
