@@ -1149,18 +1149,27 @@ __global__ __launch_bounds__(1024) void combine_kernel(const _Float16* __restric
         }
     }
     __syncthreads();
-    if (t < 32) {
+    // waves 0..3: lane l of wave w takes head 8w + l % 8 and splits l / 8,
+    // l / 8 + 8, ...; the eight lanes of a head then meet by shuffles
+    if (t < 256) {
+        const int h = 8 * (t >> 6) + (t & 7), s0 = (t & 63) >> 3;
         float mstar = -__builtin_inff();
-        for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, wgt[s][t]);
+        for (int s = s0; s < splits; s += 8) mstar = fmaxf(mstar, wgt[s][h]);
+        mstar = fmaxf(mstar, __shfl_xor(mstar, 8));
+        mstar = fmaxf(mstar, __shfl_xor(mstar, 16));
+        mstar = fmaxf(mstar, __shfl_xor(mstar, 32));
         float den = 0.0f;
-        for (int s = 0; s < splits; ++s) {
-            const float ms = wgt[s][t];
+        for (int s = s0; s < splits; s += 8) {
+            const float ms = wgt[s][h];
             const float w = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mstar);
             // a split's partial is its output divided by its row sum
-            wgt[s][t] = w * lsum[s][t];
-            den += w * lsum[s][t];
+            wgt[s][h] = w * lsum[s][h];
+            den += w * lsum[s][h];
         }
-        inv_den[t] = den > 0.0f ? 1.0f / den : 0.0f;
+        den += __shfl_xor(den, 8);
+        den += __shfl_xor(den, 16);
+        den += __shfl_xor(den, 32);
+        if ((t & 63) < 8) inv_den[h] = den > 0.0f ? 1.0f / den : 0.0f;
     }
     __syncthreads();
     auto emit = [&](int j, float num, bool first) {
